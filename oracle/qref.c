@@ -1,0 +1,437 @@
+/*
+ * qref.c -- the CPU oracle for GGUF block dequantisation, the fused
+ * dequantise-and-dot GEMV and the stacked-expert MoE FFN.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path links, loads or
+ * calls this file: only the test-suite, the smoke check and the CPU
+ * baseline leg of the benchmark do.  It shares no code, header, table or
+ * constant with the HIP library.
+ *
+ * Style: plain, slow, single-threaded, obviously correct.  Every weight is
+ * decoded element by element from its own index formula into a double,
+ * every dot product is accumulated in double in ascending column order.
+ * Built with -ffp-contract=off so no fused multiply-add changes a rounding.
+ *
+ * Sources (web pages; the item named is where the definition sits):
+ *   [gpu.rs]   docs.rs, crate ferrox-cuda 0.14.0, source src/gpu.rs
+ *   [wm.rs]    docs.rs, ferrox-core 0.16.0, src/ferrox_core/weight_matrix.rs
+ *   [moe.rs]   docs.rs, crate aprender-serve 0.70.2, source
+ *              src/gguf/cuda/forward_qwen3_moe_resident.rs
+ *
+ * Parity pins for every function are in tests/test_oracle_*.py.  Readings
+ * taken where the pages are silent are marked READING below.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Format tags: ggml's numeric type ids for the five block formats plus F32
+ * ([wm.rs] QuantKind / quant_kind_for map GGUF dtypes onto these kinds). */
+#define QREF_F32 0
+#define QREF_Q4_0 2
+#define QREF_Q8_0 8
+#define QREF_Q4_K 12
+#define QREF_Q5_K 13
+#define QREF_Q6_K 14
+
+#define QREF_OK 0
+#define QREF_EINVAL 1
+#define QREF_EUNSUPPORTED 2
+
+/* Elements per block and bytes per block.
+ * [gpu.rs] Q8_0_MATVEC_KERNEL_SRC: 34-byte blocks of 32 values.
+ * [gpu.rs] Q4_0_MATVEC_KERNEL_SRC: 18-byte blocks of 32 values.
+ * [gpu.rs] Q4_K_MATVEC_KERNEL_SRC: 144-byte super-blocks of 256 values.
+ * [gpu.rs] Q5_K_MATVEC_KERNEL_SRC: 176-byte super-blocks of 256 values.
+ * [gpu.rs] Q6_K_MATVEC_KERNEL_SRC: 210-byte super-blocks of 256 values.
+ * F32 is one 4-byte value per element. */
+int qref_block_elems(int fmt) {
+    switch (fmt) {
+    case QREF_F32: return 1;
+    case QREF_Q4_0: return 32;
+    case QREF_Q8_0: return 32;
+    case QREF_Q4_K: return 256;
+    case QREF_Q5_K: return 256;
+    case QREF_Q6_K: return 256;
+    default: return 0;
+    }
+}
+
+int qref_block_bytes(int fmt) {
+    switch (fmt) {
+    case QREF_F32: return 4;
+    case QREF_Q4_0: return 18;
+    case QREF_Q8_0: return 34;
+    case QREF_Q4_K: return 144;
+    case QREF_Q5_K: return 176;
+    case QREF_Q6_K: return 210;
+    default: return 0;
+    }
+}
+
+/* Bytes of one row: whole blocks, no padding ([wm.rs] block_bytes_per_row).
+ * Returns -1 when cols is not a positive multiple of the block size. */
+int64_t qref_row_bytes(int fmt, int64_t cols) {
+    int qk = qref_block_elems(fmt);
+    if (qk == 0 || cols <= 0 || cols % qk != 0) return -1;
+    return (cols / qk) * (int64_t)qref_block_bytes(fmt);
+}
+
+/* IEEE binary16 -> double, written from the bit layout.
+ * [gpu.rs] ferrox_f16_to_f32: sign bit 15, 5-bit exponent, 10-bit fraction;
+ * exponent 0 is subnormal (fraction * 2^-24), exponent 31 is infinity when
+ * the fraction is 0 and NaN otherwise, any other exponent gives
+ * (1024 + fraction) * 2^(exponent - 25).  The sign is applied last. */
+double qref_f16(uint16_t h) {
+    unsigned sign = (h >> 15) & 1u;
+    unsigned expo = (h >> 10) & 31u;
+    unsigned frac = h & 1023u;
+    double v;
+    if (expo == 0) {
+        v = ldexp((double)frac, -24);
+    } else if (expo == 31) {
+        v = frac ? NAN : INFINITY;
+    } else {
+        v = ldexp((double)(1024u + frac), (int)expo - 25);
+    }
+    return sign ? -v : v;
+}
+
+/* Little-endian 16-bit field at byte offset off of a block. */
+static uint16_t le16(const uint8_t *p, int off) {
+    return (uint16_t)(p[off] | (p[off + 1] << 8));
+}
+
+/* Q4_K / Q5_K 6-bit (scale, min) pair of sub-block s (0..7) from the 12
+ * packed bytes S.  [gpu.rs] ferrox_q4_k_scale_min: for s < 4 the low six
+ * bits of S[s] and S[s+4]; for s >= 4 the low nibble (scale) or high nibble
+ * (min) of S[s+4] supplies bits 0..3 and the top two bits of S[s-4] (scale)
+ * or S[s] (min) supply bits 4..5. */
+static void kquant_scale_min(const uint8_t *S, int s, int *sc, int *m) {
+    if (s < 4) {
+        *sc = S[s] & 63;
+        *m = S[s + 4] & 63;
+    } else {
+        *sc = (S[s + 4] & 15) + 16 * (S[s - 4] >> 6);
+        *m = (S[s + 4] >> 4) + 16 * (S[s] >> 6);
+    }
+}
+
+/* Dequantise one block of format fmt into out[block_elems]. */
+int qref_dequant_block(int fmt, const uint8_t *blk, double *out) {
+    int e;
+    switch (fmt) {
+    case QREF_F32: {
+        float f;
+        memcpy(&f, blk, 4);
+        out[0] = (double)f;
+        return QREF_OK;
+    }
+    case QREF_Q8_0: {
+        /* [gpu.rs] Q8_0_MATVEC_KERNEL_SRC: f16 scale d at bytes 0..1, then
+         * 32 signed bytes; value i = d * q_i. */
+        double d = qref_f16(le16(blk, 0));
+        for (e = 0; e < 32; e++) out[e] = d * (double)(int8_t)blk[2 + e];
+        return QREF_OK;
+    }
+    case QREF_Q4_0: {
+        /* [gpu.rs] Q4_0_MATVEC_KERNEL_SRC: f16 d at 0..1, 16 packed bytes
+         * from byte 2; element j < 16 is the low nibble of byte j, element
+         * j + 16 the high nibble; value = d * (nibble - 8). */
+        double d = qref_f16(le16(blk, 0));
+        for (e = 0; e < 32; e++) {
+            uint8_t byte = blk[2 + (e % 16)];
+            int nib = (e < 16) ? (byte & 15) : (byte >> 4);
+            out[e] = d * (double)(nib - 8);
+        }
+        return QREF_OK;
+    }
+    case QREF_Q4_K: {
+        /* [gpu.rs] Q4_K_MATVEC_KERNEL_SRC: d (f16) at 0, dmin (f16) at 2,
+         * 12 scale bytes at 4, 128 quant bytes at 16.  Element e belongs to
+         * sub-block s = e/32 with its own (sc, m).  Its 4-bit code lives in
+         * qs[32*(e/64) + e%32]: the low nibble for the first 32 elements of
+         * each 64, the high nibble for the second 32.
+         * value = d*sc*q - dmin*m.  READING: the code (8 sub-blocks of 32)
+         * decides over the page's prose that speaks of 4 sub-blocks of 64. */
+        double d = qref_f16(le16(blk, 0));
+        double dmin = qref_f16(le16(blk, 2));
+        const uint8_t *S = blk + 4, *qs = blk + 16;
+        for (e = 0; e < 256; e++) {
+            int s = e / 32, sc, m;
+            int p = e / 64, hi = (e % 64) / 32, l = e % 32;
+            uint8_t byte = qs[32 * p + l];
+            int q = hi ? (byte >> 4) : (byte & 15);
+            kquant_scale_min(S, s, &sc, &m);
+            out[e] = d * (double)sc * (double)q - dmin * (double)m;
+        }
+        return QREF_OK;
+    }
+    case QREF_Q5_K: {
+        /* [gpu.rs] Q5_K_MATVEC_KERNEL_SRC: as Q4_K, with 32 high-bit bytes
+         * qh at 16 and the 128 quant bytes at 48.  The fifth bit of element
+         * e is bit (2*(e/64) + (e%64)/32) of qh[e%32]; q = nibble + 16*bit. */
+        double d = qref_f16(le16(blk, 0));
+        double dmin = qref_f16(le16(blk, 2));
+        const uint8_t *S = blk + 4, *qh = blk + 16, *qs = blk + 48;
+        for (e = 0; e < 256; e++) {
+            int s = e / 32, sc, m;
+            int p = e / 64, hi = (e % 64) / 32, l = e % 32;
+            uint8_t byte = qs[32 * p + l];
+            int nib = hi ? (byte >> 4) : (byte & 15);
+            int bit = (qh[l] >> (2 * p + hi)) & 1;
+            int q = nib + 16 * bit;
+            kquant_scale_min(S, s, &sc, &m);
+            out[e] = d * (double)sc * (double)q - dmin * (double)m;
+        }
+        return QREF_OK;
+    }
+    case QREF_Q6_K: {
+        /* [gpu.rs] Q6_K_MATVEC_KERNEL_SRC: ql[128] at 0, qh[64] at 128,
+         * sixteen signed int8 scales at 192, f16 d at 208.  The block is two
+         * halves of 128; within half h element e has t = (e%128)/32 and
+         * l = e%32.  Its low four bits are nibble (t/2) of
+         * ql[64h + 32*(t%2) + l], its top two bits are bits 2t..2t+1 of
+         * qh[32h + l]; q = low + 16*top; value = d * sc[e/16] * (q - 32),
+         * the scale read as SIGNED (the page records that an unsigned read
+         * was a bug). */
+        double d = qref_f16(le16(blk, 208));
+        const uint8_t *ql = blk, *qh = blk + 128;
+        const int8_t *sc = (const int8_t *)(blk + 192);
+        for (e = 0; e < 256; e++) {
+            int h = e / 128, t = (e % 128) / 32, l = e % 32;
+            uint8_t lb = ql[64 * h + 32 * (t % 2) + l];
+            int low = (t / 2) ? (lb >> 4) : (lb & 15);
+            int top = (qh[32 * h + l] >> (2 * t)) & 3;
+            int q = low + 16 * top;
+            out[e] = d * (double)sc[e / 16] * (double)(q - 32);
+        }
+        return QREF_OK;
+    }
+    default:
+        return QREF_EUNSUPPORTED;
+    }
+}
+
+/* Dequantise one row of cols elements. */
+int qref_dequant_row(int fmt, const uint8_t *row, int64_t cols, double *out) {
+    int64_t rb = qref_row_bytes(fmt, cols);
+    int qk = qref_block_elems(fmt), bb = qref_block_bytes(fmt);
+    int64_t b;
+    if (rb < 0) return qref_block_elems(fmt) ? QREF_EINVAL : QREF_EUNSUPPORTED;
+    for (b = 0; b < cols / qk; b++) {
+        int rc = qref_dequant_block(fmt, row + b * bb, out + b * qk);
+        if (rc) return rc;
+    }
+    return QREF_OK;
+}
+
+/* One output element: sum over c of w[c] * x[c] in double, ascending c, and
+ * the sum of |w[c] * x[c]| for the tolerance.  With the scales drawn in the
+ * synthetic workloads' ranges each decoded weight has at most 24 significant
+ * bits, so its product with an f32 activation is exact in double and the
+ * only rounding is in the sum. */
+static void dot_f64(const double *w, const float *x, int64_t cols, double *y,
+                    double *yabs) {
+    double acc = 0.0, aabs = 0.0;
+    int64_t c;
+    for (c = 0; c < cols; c++) {
+        double p = w[c] * (double)x[c];
+        acc += p;
+        aabs += fabs(p);
+    }
+    *y = acc;
+    *yabs = aabs;
+}
+
+/* GEMV over selected rows: Y[b*nidx + i] = sum_c deq(W)[row_idx[i]][c] *
+ * X[b*cols + c] for b < batch.  Layout: W row-major [rows][row_bytes],
+ * X [batch][cols], Y and Yabs [batch][nidx] ([wm.rs] apply / apply_batch:
+ * activations and outputs are batch-major).  Yabs may be NULL. */
+int qref_gemv_rows(int fmt, const void *W, int64_t rows, int64_t cols,
+                   const float *X, int batch, const int64_t *row_idx,
+                   int64_t nidx, double *Y, double *Yabs) {
+    int64_t rb = qref_row_bytes(fmt, cols), i;
+    double *w;
+    int b, rc = QREF_OK;
+    if (rb < 0) return qref_block_elems(fmt) ? QREF_EINVAL : QREF_EUNSUPPORTED;
+    if (!W || !X || !Y || rows <= 0 || batch <= 0 || nidx < 0) return QREF_EINVAL;
+    w = (double *)malloc(sizeof(double) * (size_t)cols);
+    if (!w) return QREF_EINVAL;
+    for (i = 0; i < nidx; i++) {
+        int64_t r = row_idx[i];
+        if (r < 0 || r >= rows) { rc = QREF_EINVAL; break; }
+        rc = qref_dequant_row(fmt, (const uint8_t *)W + r * rb, cols, w);
+        if (rc) break;
+        for (b = 0; b < batch; b++) {
+            double y, ya;
+            dot_f64(w, X + (int64_t)b * cols, cols, &y, &ya);
+            Y[(int64_t)b * nidx + i] = y;
+            if (Yabs) Yabs[(int64_t)b * nidx + i] = ya;
+        }
+    }
+    free(w);
+    return rc;
+}
+
+/* Full GEMV: every row, Y and Yabs [batch][rows]. */
+int qref_gemv(int fmt, const void *W, int64_t rows, int64_t cols,
+              const float *X, int batch, double *Y, double *Yabs) {
+    int64_t *idx, r;
+    int rc;
+    if (rows <= 0) return QREF_EINVAL;
+    idx = (int64_t *)malloc(sizeof(int64_t) * (size_t)rows);
+    if (!idx) return QREF_EINVAL;
+    for (r = 0; r < rows; r++) idx[r] = r;
+    rc = qref_gemv_rows(fmt, W, rows, cols, X, batch, idx, rows, Y, Yabs);
+    free(idx);
+    return rc;
+}
+
+/* Rank order of experts: a comes before b when its logit is larger; equal
+ * logits go to the lower index; a NaN logit ranks below every number
+ * (READING: the routing function's body is not on the pages; the lower-index
+ * tie-break is the stated rule, NaN placement is ours). */
+static int ranks_before(const double *l, int a, int b) {
+    int na = isnan(l[a]), nb = isnan(l[b]);
+    if (na != nb) return nb; /* the non-NaN one first */
+    if (!na && l[a] != l[b]) return l[a] > l[b];
+    return a < b;
+}
+
+/* Routing: softmax over all E logits, top-k, renormalise over the chosen k
+ * ([moe.rs] module doc: router GEMV, then softmax, top-k, renormalise; the
+ * routes are reported as (expert, weight) pairs in rank order, see
+ * last_routes).  READING: the choice is made on the logits, which orders the
+ * experts exactly as the exact softmax probabilities do (exp is strictly
+ * increasing) and cannot merge two distinct values the way rounded
+ * probabilities could.  Weights: p = softmax(l) in double with the maximum
+ * subtracted, w_s = p[sel_s] / sum over the k chosen of p.
+ * sel[k] int32, w[k] double, both in rank order. */
+int qref_route(const double *logits, int n_experts, int top_k, int32_t *sel,
+               double *w) {
+    int i, j, s;
+    double mx = -INFINITY, denom = 0.0, ssum = 0.0;
+    double *p;
+    if (!logits || !sel || !w || n_experts <= 0 || top_k <= 0 || top_k > n_experts)
+        return QREF_EINVAL;
+    /* selection by repeated "best not yet taken" scan: O(k * E) */
+    for (s = 0; s < top_k; s++) {
+        int best = -1;
+        for (i = 0; i < n_experts; i++) {
+            int taken = 0;
+            for (j = 0; j < s; j++)
+                if (sel[j] == i) taken = 1;
+            if (taken) continue;
+            if (best < 0 || ranks_before(logits, i, best)) best = i;
+        }
+        sel[s] = best;
+    }
+    p = (double *)malloc(sizeof(double) * (size_t)n_experts);
+    if (!p) return QREF_EINVAL;
+    for (i = 0; i < n_experts; i++)
+        if (logits[i] > mx) mx = logits[i];
+    for (i = 0; i < n_experts; i++) {
+        p[i] = exp(logits[i] - mx);
+        denom += p[i];
+    }
+    for (i = 0; i < n_experts; i++) p[i] /= denom;
+    for (s = 0; s < top_k; s++) ssum += p[sel[s]];
+    for (s = 0; s < top_k; s++) w[s] = p[sel[s]] / ssum;
+    free(p);
+    return QREF_OK;
+}
+
+/* SiLU, in double.  [gpu.rs] SILU_MUL_KERNEL_SRC: silu(g) = g / (1 + e^-g),
+ * and SwiGLU is silu(gate) * up. */
+double qref_silu(double g) { return g / (1.0 + exp(-g)); }
+
+/* The stacked-expert MoE FFN for one token ([moe.rs] moe_layer and the
+ * module doc):
+ *   logits[e] = sum_i R[e][i] * x[i]                 (router, F32 weights)
+ *   (sel, w)  = route(logits, k)
+ *   for each slot s in rank order, expert e = sel[s]:
+ *     g = G[e] x,  u = U[e] x                        (rows F, cols H)
+ *     act[s][j] = w_s * silu(g_j) * u_j              (weight folded into the
+ *                                                     activation before the
+ *                                                     linear down GEMV)
+ *   y = residual + sum_s D[e] act[s]                  (down: rows H, cols F)
+ * Expert e of a stack starts at base + e * rows * row_bytes ([moe.rs]
+ * ExpertStack::expert).  Outputs (any may be NULL except y): logits[E],
+ * sel[k], w[k], act[k][F], bound[H] = |residual| + sum_s sum_j |D act|. */
+int qref_moe_ffn(const float *x, const float *residual, const float *router,
+                 int gate_fmt, const void *gate, int up_fmt, const void *up,
+                 int down_fmt, const void *down, int64_t hidden,
+                 int64_t n_experts, int64_t top_k, int64_t expert_dim,
+                 double *y, double *bound, double *logits_out,
+                 int32_t *sel_out, double *w_out, double *act_out) {
+    int64_t H = hidden, E = n_experts, K = top_k, F = expert_dim;
+    int64_t rb_g = qref_row_bytes(gate_fmt, H), rb_u = qref_row_bytes(up_fmt, H);
+    int64_t rb_d = qref_row_bytes(down_fmt, F);
+    int64_t e, s, j, r;
+    int rc = QREF_OK;
+    double *logits, *w, *act, *row, *g, *u;
+    int32_t *sel;
+    if (!x || !residual || !router || !gate || !up || !down || !y) return QREF_EINVAL;
+    if (H <= 0 || E <= 0 || K <= 0 || F <= 0 || K > E) return QREF_EINVAL;
+    if (rb_g < 0 || rb_u < 0 || rb_d < 0) return QREF_EUNSUPPORTED;
+    logits = (double *)malloc(sizeof(double) * (size_t)E);
+    w = (double *)malloc(sizeof(double) * (size_t)K);
+    sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    act = (double *)malloc(sizeof(double) * (size_t)(K * F));
+    row = (double *)malloc(sizeof(double) * (size_t)(H > F ? H : F));
+    g = (double *)malloc(sizeof(double) * (size_t)F);
+    u = (double *)malloc(sizeof(double) * (size_t)F);
+    if (!logits || !w || !sel || !act || !row || !g || !u) { rc = QREF_EINVAL; goto done; }
+
+    /* router GEMV: F32 weights [E][H] */
+    for (e = 0; e < E; e++) {
+        double yabs;
+        rc = qref_dequant_row(QREF_F32, (const uint8_t *)router + e * H * 4, H, row);
+        if (rc) goto done;
+        dot_f64(row, x, H, &logits[e], &yabs);
+    }
+    rc = qref_route(logits, (int)E, (int)K, sel, w);
+    if (rc) goto done;
+
+    /* gate, up, SwiGLU times the route weight */
+    for (s = 0; s < K; s++) {
+        const uint8_t *gb = (const uint8_t *)gate + (int64_t)sel[s] * F * rb_g;
+        const uint8_t *ub = (const uint8_t *)up + (int64_t)sel[s] * F * rb_u;
+        for (j = 0; j < F; j++) {
+            double yabs;
+            rc = qref_dequant_row(gate_fmt, gb + j * rb_g, H, row);
+            if (rc) goto done;
+            dot_f64(row, x, H, &g[j], &yabs);
+            rc = qref_dequant_row(up_fmt, ub + j * rb_u, H, row);
+            if (rc) goto done;
+            dot_f64(row, x, H, &u[j], &yabs);
+        }
+        for (j = 0; j < F; j++) act[s * F + j] = w[s] * qref_silu(g[j]) * u[j];
+    }
+
+    /* down GEMV per slot, added into the residual in rank order */
+    for (r = 0; r < H; r++) {
+        double acc = (double)residual[r], aabs = fabs((double)residual[r]);
+        for (s = 0; s < K; s++) {
+            const uint8_t *db = (const uint8_t *)down + (int64_t)sel[s] * H * rb_d;
+            rc = qref_dequant_row(down_fmt, db + r * rb_d, F, row);
+            if (rc) goto done;
+            for (j = 0; j < F; j++) {
+                double p = row[j] * act[s * F + j];
+                acc += p;
+                aabs += fabs(p);
+            }
+        }
+        y[r] = acc;
+        if (bound) bound[r] = aabs;
+    }
+    if (logits_out) memcpy(logits_out, logits, sizeof(double) * (size_t)E);
+    if (sel_out) memcpy(sel_out, sel, sizeof(int32_t) * (size_t)K);
+    if (w_out) memcpy(w_out, w, sizeof(double) * (size_t)K);
+    if (act_out) memcpy(act_out, act, sizeof(double) * (size_t)(K * F));
+done:
+    free(logits); free(w); free(sel); free(act); free(row); free(g); free(u);
+    return rc;
+}
