@@ -1,0 +1,477 @@
+// qg_api.hip -- host side of the C ABI declared in include/qgemv.h:
+// argument validation (before any HIP call), kernel selection and launch on
+// the caller's stream.  No allocation, no host synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/qgemv.h"
+#include "qg_kernels.hpp"
+
+using namespace qg;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return QG_OK;
+}
+
+struct Geom {
+    int elems, bytes;
+};
+
+Geom geom(int fmt) {
+    switch (fmt) {
+    case QG_F32: return {1, 4};
+    case QG_Q4_0: return {32, 18};
+    case QG_Q8_0: return {32, 34};
+    case QG_Q4_K: return {256, 144};
+    case QG_Q5_K: return {256, 176};
+    case QG_Q6_K: return {256, 210};
+    default: return {0, 0};
+    }
+}
+
+const char *fmt_name(int fmt) {
+    switch (fmt) {
+    case QG_F32: return "F32";
+    case QG_Q4_0: return "Q4_0";
+    case QG_Q8_0: return "Q8_0";
+    case QG_Q4_K: return "Q4_K";
+    case QG_Q5_K: return "Q5_K";
+    case QG_Q6_K: return "Q6_K";
+    default: return "unknown";
+    }
+}
+
+// Workgroups per launch: enough to cover every CU several times over; the
+// kernels loop over the rest.
+int max_grid() {
+    static std::atomic<int> cached{0};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v) return v;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            n > 0)
+            cus = n;
+    }
+    v = cus * 8;
+    cached.store(v, std::memory_order_relaxed);
+    return v;
+}
+
+int next_pow2(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+// Row-group shape for `tiles` tiles per row: lanes per group inside one wave
+// (power of two), or S whole waves; G groups per workgroup; block threads.
+struct Shape {
+    int lpr, S, G, threads;
+};
+
+bool shape_for(int tiles, Shape *s) {
+    if (tiles <= 64) {
+        s->lpr = next_pow2(tiles);
+        s->S = 1;
+        s->G = 256 / s->lpr;
+        s->threads = 256;
+        return true;
+    }
+    const int S = (tiles + 63) / 64;
+    if (S > 8) return false;
+    s->lpr = 64;
+    s->S = S;
+    s->G = S >= 4 ? 1 : 4 / S;
+    s->threads = 64 * S * s->G;
+    return true;
+}
+
+// ------------------------------------------------------------------- qgemv
+
+// Tile widths per format at batch B: the activations of a tile stay in
+// VGPRs, so columns-per-tile * B is kept at or below 128.
+constexpr int lw_k45(int B) { return B == 1 ? 32 : (B <= 4 ? 16 : 8); }  // CPT = 2 LW
+constexpr int lw_q6k(int B) { return B == 1 ? 16 : (B <= 4 ? 8 : 4); }   // CPT = 4 LW
+constexpr int lw_q80(int B) { return B <= 4 ? 32 : 16; }                 // CPT = LW
+constexpr int lw_q40(int B) { return B <= 4 ? 16 : 8; }                  // CPT = 2 LW
+constexpr int lw_f32max(int B) { return B == 1 ? 32 : (B <= 4 ? 16 : 8); }
+
+// Columns per tile for format fmt at batch B; F32 takes the widest tile
+// (<= its maximum) that divides cols.  0 if none.
+int gemv_cpt(int fmt, int B, int64_t cols) {
+    switch (fmt) {
+    case QG_Q4_K:
+    case QG_Q5_K: return 2 * (B == 1 ? lw_k45(1) : (B <= 4 ? lw_k45(4) : lw_k45(8)));
+    case QG_Q6_K: return 4 * (B == 1 ? lw_q6k(1) : (B <= 4 ? lw_q6k(4) : lw_q6k(8)));
+    case QG_Q8_0: return B <= 4 ? lw_q80(4) : lw_q80(8);
+    case QG_Q4_0: return 2 * (B <= 4 ? lw_q40(4) : lw_q40(8));
+    case QG_F32: {
+        const int maxw = B == 1 ? lw_f32max(1) : (B <= 4 ? lw_f32max(4) : lw_f32max(8));
+        for (int w = maxw; w >= 4; w >>= 1)
+            if (cols % w == 0) return w;
+        return 0;
+    }
+    default: return 0;
+    }
+}
+
+template <class F, int B, int U>
+int launch_gemv(GemvParams p, hipStream_t st) {
+    p.tiles = (int32_t)(p.cols / F::CPT);
+    Shape s;
+    if (!shape_for(p.tiles, &s))
+        return fail(QG_EUNSUPPORTED, "qgemv: %u columns need %d lane tiles per row at batch %d; "
+                                     "at most 512 are supported",
+                    p.cols, p.tiles, B);
+    p.lpr = s.lpr;
+    p.S = s.S;
+    p.G = s.G;
+    const int64_t per_iter = (int64_t)s.G * U;
+    int64_t iters = (p.rows + per_iter - 1) / per_iter;
+    const int grid = (int)(iters < max_grid() ? iters : max_grid());
+    hipLaunchKernelGGL((qgemv_kernel<F, B, U>), dim3(grid), dim3(s.threads), 0, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_ELAUNCH, "qgemv: launch failed: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+template <int B>
+int dispatch_gemv_b(int fmt, bool aligned, int cpt, const GemvParams &p, hipStream_t st) {
+    constexpr int U = B == 1 ? 4 : 2;
+    constexpr int K45 = lw_k45(B), Q6 = lw_q6k(B), Q8 = lw_q80(B), Q4 = lw_q40(B);
+    constexpr int FM = lw_f32max(B);
+    switch (fmt) {
+    case QG_Q4_K:
+        return aligned ? launch_gemv<FmtQ4K<K45, false>, B, U>(p, st)
+                       : launch_gemv<FmtQ4K<K45, true>, B, U>(p, st);
+    case QG_Q5_K:
+        return aligned ? launch_gemv<FmtQ5K<K45, false>, B, U>(p, st)
+                       : launch_gemv<FmtQ5K<K45, true>, B, U>(p, st);
+    case QG_Q6_K: return launch_gemv<FmtQ6K<Q6>, B, U>(p, st);
+    case QG_Q8_0: return launch_gemv<FmtQ80<Q8>, B, U>(p, st);
+    case QG_Q4_0: return launch_gemv<FmtQ40<Q4>, B, U>(p, st);
+    case QG_F32:
+        if (cpt == FM) return launch_gemv<FmtF32<FM>, B, U>(p, st);
+        if constexpr (FM > 8)
+            if (cpt == FM / 2) return launch_gemv<FmtF32<FM / 2>, B, U>(p, st);
+        if constexpr (FM > 16)
+            if (cpt == FM / 4) return launch_gemv<FmtF32<FM / 4>, B, U>(p, st);
+        if (cpt == 8) return launch_gemv<FmtF32<8>, B, U>(p, st);
+        return launch_gemv<FmtF32<4>, B, U>(p, st);
+    default: return fail(QG_EUNSUPPORTED, "qgemv: unknown format %d", fmt);
+    }
+}
+
+int dispatch_gemv(int fmt, int B, bool aligned, int64_t cols, const GemvParams &p,
+                  hipStream_t st) {
+    const int cpt = gemv_cpt(fmt, B, cols);
+    switch (B) {
+    case 1: return dispatch_gemv_b<1>(fmt, aligned, cpt, p, st);
+    case 2: return dispatch_gemv_b<2>(fmt, aligned, cpt, p, st);
+    case 3: return dispatch_gemv_b<3>(fmt, aligned, cpt, p, st);
+    case 4: return dispatch_gemv_b<4>(fmt, aligned, cpt, p, st);
+    case 5: return dispatch_gemv_b<5>(fmt, aligned, cpt, p, st);
+    case 6: return dispatch_gemv_b<6>(fmt, aligned, cpt, p, st);
+    case 7: return dispatch_gemv_b<7>(fmt, aligned, cpt, p, st);
+    case 8: return dispatch_gemv_b<8>(fmt, aligned, cpt, p, st);
+    default: return fail(QG_EUNSUPPORTED, "qgemv: batch %d outside 1..8", B);
+    }
+}
+
+bool tiles_fit(int fmt, int B, int64_t cols) {
+    const int cpt = gemv_cpt(fmt, B, cols);
+    if (cpt == 0) return false;
+    return (cols / cpt) <= 512;
+}
+
+// ------------------------------------------------------------------- MoE
+
+size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
+
+struct WsLayout {
+    size_t logits, sel, w, act, total;
+};
+
+WsLayout ws_layout(int64_t E, int64_t K, int64_t F) {
+    WsLayout l;
+    l.logits = 0;
+    l.sel = align16(8 * (size_t)E);
+    l.w = l.sel + align16(4 * (size_t)K);
+    l.act = l.w + align16(4 * (size_t)K);
+    l.total = l.act + align16(4 * (size_t)K * (size_t)F);
+    return l;
+}
+
+// columns per tile for the B = 1 kernels of the MoE chain
+int moe_cpt(int fmt) {
+    switch (fmt) {
+    case QG_Q4_K:
+    case QG_Q5_K:
+    case QG_Q6_K: return 64;
+    case QG_Q8_0:
+    case QG_Q4_0: return 32;
+    default: return 0;
+    }
+}
+
+template <class F>
+int launch_gateup(MoeParams p, hipStream_t st) {
+    constexpr int U = 2;
+    Shape s;
+    p.gu_tiles = p.H / F::CPT;
+    if (!shape_for(p.gu_tiles, &s))
+        return fail(QG_EUNSUPPORTED, "moe_ffn: hidden %d too wide for the gate/up kernel", p.H);
+    p.gu_lpr = s.lpr;
+    p.gu_S = s.S;
+    p.gu_G = s.G;
+    const int64_t tasks = (int64_t)p.K * p.F, per = (int64_t)s.G * U;
+    const int64_t iters = (tasks + per - 1) / per;
+    const int grid = (int)(iters < max_grid() ? iters : max_grid());
+    hipLaunchKernelGGL((moe_gateup_kernel<F, U>), dim3(grid), dim3(s.threads), 0, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(QG_ELAUNCH, "moe_ffn: gate/up launch failed: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+template <class F>
+int launch_down(MoeParams p, hipStream_t st) {
+    constexpr int U = 2;
+    Shape s;
+    p.dn_tiles_per_slot = p.F / F::CPT;
+    p.dn_tiles = p.K * p.dn_tiles_per_slot;
+    if (!shape_for(p.dn_tiles, &s))
+        return fail(QG_EUNSUPPORTED, "moe_ffn: top_k * expert_dim too wide for the down kernel");
+    p.dn_lpr = s.lpr;
+    p.dn_S = s.S;
+    p.dn_G = s.G;
+    const int64_t per = (int64_t)s.G * U;
+    const int64_t iters = (p.H + per - 1) / per;
+    const int grid = (int)(iters < max_grid() ? iters : max_grid());
+    hipLaunchKernelGGL((moe_down_kernel<F, U>), dim3(grid), dim3(s.threads), 0, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(QG_ELAUNCH, "moe_ffn: down launch failed: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+int dispatch_gateup(int fmt, const MoeParams &p, hipStream_t st) {
+    switch (fmt) {
+    case QG_Q4_K: return launch_gateup<FmtQ4K<32, true>>(p, st);
+    case QG_Q5_K: return launch_gateup<FmtQ5K<32, true>>(p, st);
+    case QG_Q6_K: return launch_gateup<FmtQ6K<16>>(p, st);
+    case QG_Q8_0: return launch_gateup<FmtQ80<32>>(p, st);
+    case QG_Q4_0: return launch_gateup<FmtQ40<16>>(p, st);
+    default: return fail(QG_EUNSUPPORTED, "moe_ffn: gate/up format %d", fmt);
+    }
+}
+
+int dispatch_down(int fmt, const MoeParams &p, hipStream_t st) {
+    switch (fmt) {
+    case QG_Q4_K: return launch_down<FmtQ4K<32, true>>(p, st);
+    case QG_Q5_K: return launch_down<FmtQ5K<32, true>>(p, st);
+    case QG_Q6_K: return launch_down<FmtQ6K<16>>(p, st);
+    case QG_Q8_0: return launch_down<FmtQ80<32>>(p, st);
+    case QG_Q4_0: return launch_down<FmtQ40<16>>(p, st);
+    default: return fail(QG_EUNSUPPORTED, "moe_ffn: down format %d", fmt);
+    }
+}
+
+bool aligned_to(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+}  // namespace
+
+// ========================================================================= ABI
+
+extern "C" {
+
+int qg_block_elems(int fmt) { return geom(fmt).elems; }
+
+int qg_block_bytes(int fmt) { return geom(fmt).bytes; }
+
+int64_t qg_row_bytes(int fmt, int64_t cols) {
+    const Geom g = geom(fmt);
+    if (g.elems == 0 || cols <= 0 || cols % g.elems != 0) return -1;
+    return (cols / g.elems) * g.bytes;
+}
+
+const char *qg_last_error(void) { return g_err; }
+
+int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
+          int batch, void *stream) {
+    const Geom g = geom(fmt);
+    if (g.elems == 0) return fail(QG_EUNSUPPORTED, "qgemv: unknown format %d", fmt);
+    if (!W || !X || !Y) return fail(QG_EINVAL, "qgemv: W, X and Y must be non-NULL");
+    if (rows <= 0 || cols <= 0)
+        return fail(QG_EINVAL, "qgemv: rows (%lld) and cols (%lld) must be positive",
+                    (long long)rows, (long long)cols);
+    if (cols % g.elems != 0)
+        return fail(QG_EUNSUPPORTED, "qgemv: %s needs cols to be a multiple of %d (got %lld)",
+                    fmt_name(fmt), g.elems, (long long)cols);
+    if (batch < 1 || batch > 8) return fail(QG_EUNSUPPORTED, "qgemv: batch %d outside 1..8", batch);
+    if (!aligned_to(W, fmt == QG_F32 ? 4 : 2))
+        return fail(QG_EINVAL, "qgemv: W is not %d-byte aligned", fmt == QG_F32 ? 4 : 2);
+    if (!aligned_to(X, 4) || !aligned_to(Y, 4))
+        return fail(QG_EINVAL, "qgemv: X and Y must be 4-byte aligned");
+    if (rows >= ((int64_t)1 << 31)) return fail(QG_EUNSUPPORTED, "qgemv: rows must be < 2^31");
+    if (cols > 65536) return fail(QG_EUNSUPPORTED, "qgemv: cols must be <= 65536");
+    if (fmt == QG_F32 && cols % 4 != 0)
+        return fail(QG_EUNSUPPORTED, "qgemv: F32 rows must be a multiple of 4 floats");
+    const int64_t rb = qg_row_bytes(fmt, cols);
+    // Batches too wide for VGPR-resident activations run as several narrower
+    // launches over column slices of X and Y.
+    int chunk = batch;
+    while (chunk > 1 && !tiles_fit(fmt, chunk, cols)) chunk = chunk > 4 ? 4 : chunk / 2;
+    if (!tiles_fit(fmt, chunk, cols))
+        return fail(QG_EUNSUPPORTED, "qgemv: %lld columns of %s exceed the kernel's row width",
+                    (long long)cols, fmt_name(fmt));
+    const bool aligned = aligned_to(W, 4) && rb % 4 == 0;
+    hipStream_t st = (hipStream_t)stream;
+    for (int b0 = 0; b0 < batch; b0 += chunk) {
+        const int nb = batch - b0 < chunk ? batch - b0 : chunk;
+        GemvParams p{};
+        p.W = (const uint8_t *)W;
+        p.X = X + (int64_t)b0 * cols;
+        p.Y = Y + (int64_t)b0 * rows;
+        p.rows = rows;
+        p.w_bytes = (uint64_t)rows * (uint64_t)rb;
+        p.row_bytes = (uint32_t)rb;
+        p.cols = (uint32_t)cols;
+        p.batch_x = (uint32_t)nb;
+        const int rc = dispatch_gemv(fmt, nb, aligned, cols, p, st);
+        if (rc != QG_OK) return rc;
+    }
+    return ok();
+}
+
+size_t moe_ffn_workspace_bytes(int64_t n_experts, int64_t top_k, int64_t expert_dim) {
+    if (n_experts <= 0 || top_k <= 0 || expert_dim <= 0 || top_k > n_experts) return 0;
+    return ws_layout(n_experts, top_k, expert_dim).total;
+}
+
+int qg_route_topk(const double *logits, int64_t n_experts, int64_t top_k, int32_t *sel_experts,
+                  float *sel_weights, void *stream) {
+    if (!logits || !sel_experts || !sel_weights)
+        return fail(QG_EINVAL, "qg_route_topk: logits, sel_experts and sel_weights are required");
+    if (n_experts <= 0 || top_k <= 0 || top_k > n_experts)
+        return fail(QG_EINVAL, "qg_route_topk: need 0 < top_k <= n_experts");
+    if (n_experts > kMaxExperts || top_k > kMaxTopK)
+        return fail(QG_EUNSUPPORTED, "qg_route_topk: n_experts <= %d and top_k <= %d",
+                    kMaxExperts, kMaxTopK);
+    if (!aligned_to(logits, 8) || !aligned_to(sel_experts, 4) || !aligned_to(sel_weights, 4))
+        return fail(QG_EINVAL, "qg_route_topk: misaligned pointer");
+    hipLaunchKernelGGL(route_topk_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, logits,
+                       (int)n_experts, (int)top_k, (int *)sel_experts, sel_weights);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(QG_ELAUNCH, "qg_route_topk: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int moe_ffn(const float *x, const float *residual, float *y, const float *router, int gate_fmt,
+            const void *gate, int up_fmt, const void *up, int down_fmt, const void *down,
+            int64_t hidden, int64_t n_experts, int64_t top_k, int64_t expert_dim,
+            int32_t *sel_experts, float *sel_weights, void *workspace, size_t workspace_bytes,
+            void *stream) {
+    if (!x || !residual || !y || !router || !gate || !up || !down || !workspace)
+        return fail(QG_EINVAL, "moe_ffn: x, residual, y, router, gate, up, down and workspace "
+                               "must be non-NULL");
+    if (hidden <= 0 || n_experts <= 0 || top_k <= 0 || expert_dim <= 0)
+        return fail(QG_EINVAL, "moe_ffn: sizes must be positive");
+    if (top_k > n_experts) return fail(QG_EINVAL, "moe_ffn: top_k %lld > n_experts %lld",
+                                       (long long)top_k, (long long)n_experts);
+    if (n_experts > kMaxExperts || top_k > kMaxTopK)
+        return fail(QG_EUNSUPPORTED, "moe_ffn: n_experts <= %d and top_k <= %d", kMaxExperts,
+                    kMaxTopK);
+    if (hidden > 65536 || expert_dim > 65536)
+        return fail(QG_EUNSUPPORTED, "moe_ffn: hidden and expert_dim must be <= 65536");
+    const Geom gg = geom(gate_fmt), gu = geom(up_fmt), gd = geom(down_fmt);
+    if (gg.elems == 0 || gu.elems == 0 || gd.elems == 0 || gate_fmt == QG_F32 ||
+        up_fmt == QG_F32 || down_fmt == QG_F32)
+        return fail(QG_EUNSUPPORTED, "moe_ffn: expert stacks must use a block format");
+    if (gate_fmt != up_fmt)
+        return fail(QG_EUNSUPPORTED, "moe_ffn: gate (%s) and up (%s) must share a format",
+                    fmt_name(gate_fmt), fmt_name(up_fmt));
+    if (hidden % gg.elems != 0 || expert_dim % gd.elems != 0)
+        return fail(QG_EUNSUPPORTED, "moe_ffn: hidden must be a multiple of %d and expert_dim "
+                                     "of %d", gg.elems, gd.elems);
+    if (!aligned_to(gate, 2) || !aligned_to(up, 2) || !aligned_to(down, 2))
+        return fail(QG_EINVAL, "moe_ffn: weight stacks must be 2-byte aligned");
+    if (!aligned_to(x, 4) || !aligned_to(residual, 4) || !aligned_to(y, 4) ||
+        !aligned_to(router, 4) || (sel_experts && !aligned_to(sel_experts, 4)) ||
+        (sel_weights && !aligned_to(sel_weights, 4)))
+        return fail(QG_EINVAL, "moe_ffn: float and int32 arrays must be 4-byte aligned");
+    if (!aligned_to(workspace, 16)) return fail(QG_EINVAL, "moe_ffn: workspace not 16-byte aligned");
+    if (y == x) return fail(QG_EINVAL, "moe_ffn: y must not alias x");
+    const WsLayout wl = ws_layout(n_experts, top_k, expert_dim);
+    if (workspace_bytes < wl.total)
+        return fail(QG_EINVAL, "moe_ffn: workspace of %zu bytes, %zu needed", workspace_bytes,
+                    wl.total);
+    const int64_t rbg = qg_row_bytes(gate_fmt, hidden), rbd = qg_row_bytes(down_fmt, expert_dim);
+    const uint64_t gate_bytes = (uint64_t)n_experts * expert_dim * rbg;
+    const uint64_t down_bytes = (uint64_t)n_experts * hidden * rbd;
+    if (gate_bytes > 0xFFFFFFFFull || down_bytes > 0xFFFFFFFFull)
+        return fail(QG_EUNSUPPORTED, "moe_ffn: each expert stack must be under 4 GiB");
+    if (hidden % moe_cpt(gate_fmt) != 0 || expert_dim % moe_cpt(down_fmt) != 0)
+        return fail(QG_EUNSUPPORTED, "moe_ffn: sizes do not tile");
+    if (hidden / moe_cpt(gate_fmt) > 512 || top_k * (expert_dim / moe_cpt(down_fmt)) > 512)
+        return fail(QG_EUNSUPPORTED, "moe_ffn: hidden or top_k * expert_dim too large");
+
+    uint8_t *ws = (uint8_t *)workspace;
+    MoeParams p{};
+    p.x = x;
+    p.residual = residual;
+    p.y = y;
+    p.gate = (const uint8_t *)gate;
+    p.up = (const uint8_t *)up;
+    p.down = (const uint8_t *)down;
+    p.gate_bytes = gate_bytes;
+    p.up_bytes = gate_bytes;
+    p.down_bytes = down_bytes;
+    p.rb_gate = (uint32_t)rbg;
+    p.rb_down = (uint32_t)rbd;
+    p.H = (int32_t)hidden;
+    p.E = (int32_t)n_experts;
+    p.K = (int32_t)top_k;
+    p.F = (int32_t)expert_dim;
+    p.logits = (const double *)(ws + wl.logits);
+    p.ws_sel = (int32_t *)(ws + wl.sel);
+    p.ws_w = (float *)(ws + wl.w);
+    p.act = (float *)(ws + wl.act);
+    p.sel_out = sel_experts;
+    p.w_out = sel_weights;
+
+    hipStream_t st = (hipStream_t)stream;
+    hipLaunchKernelGGL(moe_router_kernel, dim3((unsigned)n_experts), dim3(64), 0, st, router, x,
+                       (int)hidden, (double *)(ws + wl.logits));
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_ELAUNCH, "moe_ffn: router launch failed: %s",
+                                     hipGetErrorString(e));
+    int rc = dispatch_gateup(gate_fmt, p, st);
+    if (rc != QG_OK) return rc;
+    rc = dispatch_down(down_fmt, p, st);
+    if (rc != QG_OK) return rc;
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,448 @@
+// qg_kernels.hpp -- the gfx950 kernels: the batched dequantise-and-dot GEMV
+// and the three kernels of the stacked-expert MoE FFN.
+//
+// GEMV work layout.  A "row group" of lanes covers one weight row: lane g of
+// the group owns tile g (a fixed column set, see qg_formats.hpp), holds its
+// activations for all B batch columns in VGPRs, and walks rows.  A group is
+// `lpr` lanes of one wave (a power of two <= 64) or S whole waves.  Every
+// iteration a workgroup takes G*U consecutive rows, group g rows
+// [g*U, g*U+U): all U rows' loads are issued before any is used.  Partial
+// sums are reduced inside the wave with DPP / swizzle / bpermute and, for
+// S > 1, across the group's waves through LDS, in a fixed order.
+//
+// MoE (web page: docs.rs, crate aprender-serve 0.70.2, source
+// src/gguf/cuda/forward_qwen3_moe_resident.rs -- module doc and moe_layer):
+//   K1 moe_router_kernel   logits[e] = R[e] . x in f64, one wave per expert
+//   K2 moe_gateup_kernel   every workgroup ranks the logits (softmax, top-k,
+//                          renormalise, ties to the lower index); then row
+//                          tasks (slot s, row j) compute g = G[e_s][j] . x
+//                          and u = U[e_s][j] . x and store
+//                          a[s][j] = w_s * silu(g) * u
+//   K3 moe_down_kernel     y[r] = residual[r] + sum_s D[e_s][r] . a[s]; the
+//                          lanes of a row group own (slot, tile) pairs
+#pragma once
+
+#include "qg_formats.hpp"
+
+namespace qg {
+
+struct GemvParams {
+    const uint8_t *W;
+    const float *X;
+    float *Y;
+    int64_t rows;
+    uint64_t w_bytes;    // rows * row_bytes
+    uint32_t row_bytes;
+    uint32_t cols;
+    uint32_t batch_x;    // X rows present (>= B is not required: B <= batch_x)
+    int32_t tiles;       // tiles per row
+    int32_t lpr;         // lanes per row group inside a wave (S == 1)
+    int32_t S;           // waves per row group
+    int32_t G;           // row groups per workgroup
+};
+
+// Buffer resource for the weight bytes from byte `start` of W to the end
+// (w_bytes): base rounded down to 4 bytes, *delta = bytes between that base
+// and W + start.  The record count is rounded up to a whole dword: a dword
+// that only partly overlaps the array is read whole (its other bytes lie in
+// the same page), while the hardware returns zero for a dword that overlaps
+// the record range only in part.
+__device__ __forceinline__ rsrc_t rows_rsrc(const uint8_t *W, uint64_t w_bytes, uint64_t start,
+                                            uint32_t *delta) {
+    const uint8_t *base = W + start;
+    const uint8_t *abase = (const uint8_t *)((uintptr_t)base & ~(uintptr_t)3);
+    *delta = (uint32_t)(base - abase);
+    const uint64_t rem = (w_bytes - start + *delta + 3) & ~(uint64_t)3;
+    return make_rsrc(abase, rem > 0xFFFFFFFCull ? 0xFFFFFFFCu : (uint32_t)rem);
+}
+
+template <class F, int B, int U>
+__global__ void __launch_bounds__(512) qgemv_kernel(GemvParams p) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int grp, lig;
+    if (p.S == 1) {
+        grp = wave * (64 / p.lpr) + lane / p.lpr;
+        lig = lane & (p.lpr - 1);
+    } else {
+        grp = wave / p.S;
+        lig = (wave % p.S) * 64 + lane;
+    }
+    const bool active = lig < p.tiles;
+    const typename F::Lane L = F::init(active ? lig : 0);
+
+    float x[B][F::CPT], sx[B][F::NSUM];
+    {
+        const rsrc_t rx = make_rsrc(p.X, 4u * p.cols * (uint32_t)B);
+        load_tile_x<F, B>(rx, p.cols, L, active, x, sx);
+    }
+
+    __shared__ float red[8][U * B];
+    const int64_t rpi = (int64_t)p.G * U;
+    for (int64_t it = blockIdx.x; it * rpi < p.rows; it += gridDim.x) {
+        const int64_t r0 = it * rpi;
+        uint32_t delta;
+        const rsrc_t rs = rows_rsrc(p.W, p.w_bytes, (uint64_t)r0 * p.row_bytes, &delta);
+        const int64_t rg = r0 + (int64_t)grp * U;
+
+        typename F::Raw raw[U];
+#pragma unroll
+        for (int u = 0; u < U; u++)
+            if (active && rg + u < p.rows)
+                F::load(rs, delta + (uint32_t)(grp * U + u) * p.row_bytes, L, raw[u]);
+
+        float acc[U][B];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+#pragma unroll
+            for (int b = 0; b < B; b++) acc[u][b] = 0.f;
+            if (active && rg + u < p.rows) F::template dot<B>(raw[u], L, x, sx, acc[u]);
+        }
+
+        const int width = p.S == 1 ? p.lpr : 64;
+#pragma unroll
+        for (int u = 0; u < U; u++)
+#pragma unroll
+            for (int b = 0; b < B; b++) acc[u][b] = group_sum(acc[u][b], width);
+
+        if (p.S == 1) {
+            if (lig == 0) {
+#pragma unroll
+                for (int u = 0; u < U; u++)
+                    if (rg + u < p.rows)
+#pragma unroll
+                        for (int b = 0; b < B; b++) p.Y[b * p.rows + rg + u] = acc[u][b];
+            }
+        } else {
+            if (lane == 0) {
+#pragma unroll
+                for (int u = 0; u < U; u++)
+#pragma unroll
+                    for (int b = 0; b < B; b++) red[wave][u * B + b] = acc[u][b];
+            }
+            __syncthreads();
+            if (wave % p.S == 0 && lane < U * B) {
+                float s = 0.f;
+                for (int w = 0; w < p.S; w++) s += red[wave + w][lane];
+                const int u = lane / B, b = lane % B;
+                if (rg + u < p.rows) p.Y[b * p.rows + rg + u] = s;
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ------------------------------------------------------------------ routing
+
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 32;
+
+// Order-preserving map of a double onto an unsigned 64-bit key, returned as
+// (hi, lo) halves: larger logits give larger keys, -0.0 and +0.0 share a
+// key, and NaN maps to 0, below every number (-inf included).  Rank order:
+// a larger key first, equal keys to the lower expert index.
+__device__ __forceinline__ void order_key(double v, uint32_t *hi, uint32_t *lo) {
+    uint64_t b = __builtin_bit_cast(uint64_t, v);
+    b = (v == 0.0) ? 0ull : b;
+    uint64_t k = (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+    k = __builtin_isnan(v) ? 0ull : k;
+    *hi = (uint32_t)(k >> 32);
+    *lo = (uint32_t)k;
+}
+
+__device__ __forceinline__ bool key_before(uint32_t ah, uint32_t al, int ai, uint32_t bh,
+                                           uint32_t bl, int bi) {
+    return (ah > bh) | ((ah == bh) & ((al > bl) | ((al == bl) & (ai < bi))));
+}
+
+// One wave: softmax / top-k / renormalise over E <= 1024 f64 logits.  Lane
+// l holds the keys of experts l, l+64, ...; each of the k rounds takes the
+// best expert not yet taken (lane-local scan, then a butterfly over the
+// wave; the order is total, so every lane ends with the same winner).  All
+// selections are done on 32-bit halves with selects, never with a 64-bit
+// value carried across divergent control flow.  Weights:
+// w_s = exp(l_s - l_0) / sum_{j<k} exp(l_j - l_0), which equals the softmax
+// probabilities renormalised over the chosen set.  Lanes s < k write
+// sel[s], wout[s] (any memory space).
+__device__ void route_topk_wave(const double *__restrict__ logits, int E, int k, int *sel,
+                                float *wout) {
+    constexpr int PER = kMaxExperts / 64;
+    constexpr int NONE = 0x7FFFFFFF;
+    const int lane = __lane_id();
+    uint32_t kh[PER], kl[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const int e = lane + 64 * i;
+        const double v = logits[e < E ? e : 0];
+        order_key(v, &kh[i], &kl[i]);
+    }
+    uint32_t avail = 0;
+#pragma unroll
+    for (int i = 0; i < PER; i++) avail |= (lane + 64 * i < E) ? (1u << i) : 0u;
+
+    int chosen_e = 0;
+    for (int s = 0; s < k; s++) {
+        uint32_t bh = 0, bl = 0;
+        int bi = NONE;
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            const int e = lane + 64 * i;
+            const bool take = ((avail >> i) & 1u) && key_before(kh[i], kl[i], e, bh, bl, bi);
+            bh = take ? kh[i] : bh;
+            bl = take ? kl[i] : bl;
+            bi = take ? e : bi;
+        }
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) {
+            const uint32_t oh = (uint32_t)shfl_xor_i((int)bh, m);
+            const uint32_t ol = (uint32_t)shfl_xor_i((int)bl, m);
+            const int oi = shfl_xor_i(bi, m);
+            const bool take = key_before(oh, ol, oi, bh, bl, bi);
+            bh = take ? oh : bh;
+            bl = take ? ol : bl;
+            bi = take ? oi : bi;
+        }
+        const uint32_t mine = (lane == (bi & 63)) ? (1u << ((bi >> 6) & 31)) : 0u;
+        avail &= ~mine;
+        chosen_e = (lane == s) ? bi : chosen_e;
+    }
+    const int ce = lane < k ? chosen_e : 0;
+    const double ls = logits[ce];
+    const double l0 = __shfl(ls, 0);
+    const double ex_all = exp(ls - l0);
+    const uint64_t exb = __builtin_bit_cast(uint64_t, ex_all);
+    const uint32_t keep = lane < k ? 0xFFFFFFFFu : 0u;
+    const double ex = __builtin_bit_cast(
+        double, ((uint64_t)((uint32_t)(exb >> 32) & keep) << 32) | ((uint32_t)exb & keep));
+    const double den = wave_sum_d(ex);
+    if (lane < k) {
+        sel[lane] = chosen_e;
+        wout[lane] = (float)(ex / den);
+    }
+}
+
+__global__ void __launch_bounds__(64) route_topk_kernel(const double *logits, int E, int k,
+                                                        int *sel, float *w) {
+    route_topk_wave(logits, E, k, sel, w);
+}
+
+// ------------------------------------------------------------------ MoE K1
+
+// logits[e] = sum_i R[e][i] * x[i]: every f32*f32 product is exact in f64
+// and the sum is f64 with a fixed tree.  One wave per expert row.
+__global__ void __launch_bounds__(64) moe_router_kernel(const float *__restrict__ R,
+                                                        const float *__restrict__ x, int H,
+                                                        double *__restrict__ logits) {
+    const int e = blockIdx.x, lane = threadIdx.x;
+    const rsrc_t rr = make_rsrc(R + (int64_t)e * H, 4u * (uint32_t)H);
+    const rsrc_t rx = make_rsrc(x, 4u * (uint32_t)H);
+    double acc = 0.0;
+    // uniform trip count: columns past H read as zero through the resources
+    for (int c0 = 0; c0 < H; c0 += 256) {
+        const int c = c0 + 4 * lane;
+        uint32_t a[4], b[4];
+        load_dw<4>(rr, 4u * c, a);
+        load_dw<4>(rx, 4u * c, b);
+#pragma unroll
+        for (int j = 0; j < 4; j++)
+            acc = fma((double)__builtin_bit_cast(float, a[j]),
+                      (double)__builtin_bit_cast(float, b[j]), acc);
+    }
+    acc = wave_sum_d(acc);
+    if (lane == 0) logits[e] = acc;
+}
+
+struct MoeParams {
+    const float *x;
+    const float *residual;
+    float *y;
+    const uint8_t *gate;
+    const uint8_t *up;
+    const uint8_t *down;
+    uint64_t gate_bytes, up_bytes, down_bytes;  // whole stacks
+    uint32_t rb_gate;   // row bytes of a gate / up row (H columns)
+    uint32_t rb_down;   // row bytes of a down row (F columns)
+    int32_t H, E, K, F;
+    const double *logits;  // workspace
+    int32_t *ws_sel;       // workspace
+    float *ws_w;           // workspace
+    float *act;            // workspace [K][F]
+    int32_t *sel_out;      // optional
+    float *w_out;          // optional
+    // gate/up kernel geometry
+    int32_t gu_tiles, gu_lpr, gu_S, gu_G;
+    // down kernel geometry
+    int32_t dn_tiles_per_slot, dn_tiles, dn_lpr, dn_S, dn_G;
+};
+
+__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
+
+// ------------------------------------------------------------------ MoE K2
+
+template <class F, int U>
+__global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
+    __shared__ int s_sel[kMaxTopK];
+    __shared__ float s_w[kMaxTopK];
+    __shared__ float red[8][2 * U];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int grp, lig;
+    if (p.gu_S == 1) {
+        grp = wave * (64 / p.gu_lpr) + lane / p.gu_lpr;
+        lig = lane & (p.gu_lpr - 1);
+    } else {
+        grp = wave / p.gu_S;
+        lig = (wave % p.gu_S) * 64 + lane;
+    }
+    const bool active = lig < p.gu_tiles;
+    const typename F::Lane L = F::init(active ? lig : 0);
+    float x[1][F::CPT], sx[1][F::NSUM];
+    {
+        const rsrc_t rx = make_rsrc(p.x, 4u * (uint32_t)p.H);
+        load_tile_x<F, 1>(rx, (uint32_t)p.H, L, active, x, sx);
+    }
+    if (wave == 0) route_topk_wave(p.logits, p.E, p.K, s_sel, s_w);
+    __syncthreads();
+    if (blockIdx.x == 0 && tid < p.K) {
+        p.ws_sel[tid] = s_sel[tid];
+        p.ws_w[tid] = s_w[tid];
+        if (p.sel_out) p.sel_out[tid] = s_sel[tid];
+        if (p.w_out) p.w_out[tid] = s_w[tid];
+    }
+
+    uint32_t dg, du;
+    const rsrc_t rg = rows_rsrc(p.gate, p.gate_bytes, 0, &dg);
+    const rsrc_t ru = rows_rsrc(p.up, p.up_bytes, 0, &du);
+    const int64_t tasks = (int64_t)p.K * p.F;
+    const int64_t tpi = (int64_t)p.gu_G * U;
+    for (int64_t it = blockIdx.x; it * tpi < tasks; it += gridDim.x) {
+        const int64_t t0 = it * tpi + (int64_t)grp * U;
+        typename F::Raw rawg[U], rawu[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t t = t0 + u;
+            if (active && t < tasks) {
+                const int s = (int)(t / p.F), j = (int)(t % p.F);
+                const uint32_t off = ((uint32_t)s_sel[s] * (uint32_t)p.F + (uint32_t)j) * p.rb_gate;
+                F::load(rg, dg + off, L, rawg[u]);
+                F::load(ru, du + off, L, rawu[u]);
+            }
+        }
+        float ag[U][1], au[U][1];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            ag[u][0] = au[u][0] = 0.f;
+            if (active && t0 + u < tasks) {
+                F::template dot<1>(rawg[u], L, x, sx, ag[u]);
+                F::template dot<1>(rawu[u], L, x, sx, au[u]);
+            }
+        }
+        const int width = p.gu_S == 1 ? p.gu_lpr : 64;
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            ag[u][0] = group_sum(ag[u][0], width);
+            au[u][0] = group_sum(au[u][0], width);
+        }
+        if (p.gu_S == 1) {
+            if (lig == 0) {
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    const int64_t t = t0 + u;
+                    if (t < tasks) {
+                        const int s = (int)(t / p.F);
+                        p.act[t] = s_w[s] * silu_f(ag[u][0]) * au[u][0];
+                    }
+                }
+            }
+        } else {
+            if (lane == 0) {
+#pragma unroll
+                for (int u = 0; u < U; u++) {
+                    red[wave][2 * u] = ag[u][0];
+                    red[wave][2 * u + 1] = au[u][0];
+                }
+            }
+            __syncthreads();
+            if (wave % p.gu_S == 0 && lane < U) {
+                float g = 0.f, v = 0.f;
+                for (int w = 0; w < p.gu_S; w++) {
+                    g += red[wave + w][2 * lane];
+                    v += red[wave + w][2 * lane + 1];
+                }
+                const int64_t t = t0 + lane;
+                if (t < tasks) {
+                    const int s = (int)(t / p.F);
+                    p.act[t] = s_w[s] * silu_f(g) * v;
+                }
+            }
+            __syncthreads();
+        }
+    }
+}
+
+// ------------------------------------------------------------------ MoE K3
+
+template <class F, int U>
+__global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
+    __shared__ float red[8][U];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int grp, lig;
+    if (p.dn_S == 1) {
+        grp = wave * (64 / p.dn_lpr) + lane / p.dn_lpr;
+        lig = lane & (p.dn_lpr - 1);
+    } else {
+        grp = wave / p.dn_S;
+        lig = (wave % p.dn_S) * 64 + lane;
+    }
+    const bool active = lig < p.dn_tiles;
+    const int slot = active ? lig / p.dn_tiles_per_slot : 0;
+    const int tile = active ? lig % p.dn_tiles_per_slot : 0;
+    const typename F::Lane L = F::init(tile);
+    float x[1][F::CPT], sx[1][F::NSUM];
+    {
+        const rsrc_t ra = make_rsrc(p.act + (int64_t)slot * p.F, 4u * (uint32_t)p.F);
+        load_tile_x<F, 1>(ra, (uint32_t)p.F, L, active, x, sx);
+    }
+    const uint32_t expert_off =
+        active ? (uint32_t)p.ws_sel[slot] * (uint32_t)p.H * p.rb_down : 0u;
+    uint32_t dd;
+    const rsrc_t rd = rows_rsrc(p.down, p.down_bytes, 0, &dd);
+    const int64_t rpi = (int64_t)p.dn_G * U;
+    for (int64_t it = blockIdx.x; it * rpi < p.H; it += gridDim.x) {
+        const int64_t r0 = it * rpi + (int64_t)grp * U;
+        typename F::Raw raw[U];
+#pragma unroll
+        for (int u = 0; u < U; u++)
+            if (active && r0 + u < p.H)
+                F::load(rd, dd + expert_off + (uint32_t)(r0 + u) * p.rb_down, L, raw[u]);
+        float acc[U][1];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            acc[u][0] = 0.f;
+            if (active && r0 + u < p.H) F::template dot<1>(raw[u], L, x, sx, acc[u]);
+        }
+        const int width = p.dn_S == 1 ? p.dn_lpr : 64;
+#pragma unroll
+        for (int u = 0; u < U; u++) acc[u][0] = group_sum(acc[u][0], width);
+        if (p.dn_S == 1) {
+            if (lig == 0) {
+#pragma unroll
+                for (int u = 0; u < U; u++)
+                    if (r0 + u < p.H) p.y[r0 + u] = p.residual[r0 + u] + acc[u][0];
+            }
+        } else {
+            if (lane == 0) {
+#pragma unroll
+                for (int u = 0; u < U; u++) red[wave][u] = acc[u][0];
+            }
+            __syncthreads();
+            if (wave % p.dn_S == 0 && lane < U) {
+                float s = 0.f;
+                for (int w = 0; w < p.dn_S; w++) s += red[wave + w][lane];
+                const int64_t r = r0 + lane;
+                if (r < p.H) p.y[r] = p.residual[r] + s;
+            }
+            __syncthreads();
+        }
+    }
+}
+
+}  // namespace qg

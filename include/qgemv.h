@@ -1,0 +1,181 @@
+/*
+ * qgemv.h -- C ABI of the MI355X (gfx950) fused dequantise-and-dot library.
+ *
+ * Two operations, both computed entirely by HIP kernels on the caller's
+ * stream:
+ *
+ *   qgemv    Y = deq(W) * X for a GGUF block-quantised weight matrix W and a
+ *            small batch of f32 activation vectors.
+ *   moe_ffn  the stacked-expert mixture-of-experts FFN of one decode token:
+ *            F32 router GEMV, softmax / top-k / renormalise, then for every
+ *            routed expert a gate GEMV, an up GEMV, SwiGLU scaled by the
+ *            route weight, and a down GEMV added into the residual.
+ *
+ * Sources (web pages):
+ *   docs.rs, crate ferrox-cuda 0.14.0, source src/gpu.rs -- block layouts
+ *     (the *_MATVEC_KERNEL_SRC kernels), the f16 decoder, SwiGLU
+ *     (SILU_MUL_KERNEL_SRC), per-format launch wrappers launch_q*_matvec.
+ *   docs.rs, ferrox-core 0.16.0, weight_matrix.rs -- WeightMatrix::apply /
+ *     apply_batch (batch-major activations and outputs), block_bytes_per_row.
+ *   docs.rs, crate aprender-serve 0.70.2, source
+ *     src/gguf/cuda/forward_qwen3_moe_resident.rs -- the module doc's op
+ *     order, ExpertStack (expert e at base + e * stride), moe_layer,
+ *     last_routes.
+ *
+ * Conventions common to every entry point:
+ *   - Every array pointer is a DEVICE pointer owned by the caller.  The
+ *     library allocates nothing, frees nothing and never synchronises the
+ *     host; work is enqueued on `stream` (a hipStream_t; NULL = the default
+ *     stream) and is complete when that stream is.
+ *   - Arguments are validated on the host before any HIP call.  On error
+ *     nothing is launched, the return value is a QG_E* code and
+ *     qg_last_error() names the reason.  Input the kernels do not support is
+ *     refused, never computed approximately.
+ *   - The entry points hold no global mutable state except the thread-local
+ *     error string: calls from several host threads are safe.  Calls that
+ *     share an output buffer or a workspace must be ordered by the caller.
+ *   - Results are deterministic: no atomics take part in any sum, so the
+ *     same inputs on the same stream give the same bits.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Weight formats: ggml's numeric type ids (the pages map GGUF dtypes onto
+ * their own kinds in weight_matrix.rs quant_kind_for).  Block geometry
+ * (elements / bytes): Q4_0 32 / 18, Q8_0 32 / 34, Q4_K 256 / 144,
+ * Q5_K 256 / 176, Q6_K 256 / 210.  F32 is one little-endian float per
+ * element and is accepted for the MoE router and for qgemv. */
+enum qg_format {
+    QG_F32 = 0,
+    QG_Q4_0 = 2,
+    QG_Q8_0 = 8,
+    QG_Q4_K = 12,
+    QG_Q5_K = 13,
+    QG_Q6_K = 14
+};
+
+/* Return codes. */
+enum qg_status {
+    QG_OK = 0,
+    QG_EINVAL = 1,       /* a NULL pointer, a non-positive size, k > E, a
+                            workspace too small, a weight pointer that is
+                            not 2-byte aligned, a float pointer that is not
+                            4-byte aligned */
+    QG_EUNSUPPORTED = 2, /* an unknown format, cols not a multiple of the
+                            block size, batch outside 1..8, a size beyond the
+                            kernels' limits, a router that is not F32 */
+    QG_ELAUNCH = 3       /* the HIP runtime reported an error at launch */
+};
+
+/* Elements per block of fmt, or 0 for an unknown format. */
+int qg_block_elems(int fmt);
+
+/* Bytes per block of fmt, or 0 for an unknown format. */
+int qg_block_bytes(int fmt);
+
+/* Bytes of one row of cols elements: (cols / block_elems) * block_bytes,
+ * rows are packed with no padding (weight_matrix.rs block_bytes_per_row).
+ * Returns -1 for an unknown format or cols not a positive multiple of the
+ * block size. */
+int64_t qg_row_bytes(int fmt, int64_t cols);
+
+/* Reason for the last non-QG_OK return on the calling thread ("" if none).
+ * The string stays valid until the next call on the same thread. */
+const char *qg_last_error(void);
+
+/*
+ * qgemv: Y[b][r] = sum_c deq(W)[r][c] * X[b][c]   for b < batch, r < rows.
+ *
+ *   fmt    one of enum qg_format.
+ *   W      rows * qg_row_bytes(fmt, cols) bytes, row-major, GGUF blocks
+ *          exactly as stored in the file (no repacking).  2-byte aligned.
+ *   rows   > 0.
+ *   cols   > 0, a multiple of qg_block_elems(fmt).
+ *   X      float [batch][cols], 4-byte aligned.
+ *   Y      float [batch][rows], 4-byte aligned; must not overlap W or X.
+ *   batch  1..8.  Every weight byte is read from memory once and used for
+ *          all batch columns (weight_matrix.rs apply_batch).
+ *   stream hipStream_t or NULL.
+ *
+ * Dequantisation per element follows the block layouts of the gpu.rs page
+ * kernels; products are accumulated in f32 and reduced across lanes with a
+ * fixed tree.  Limits: rows < 2^31, cols <= 65536.
+ */
+int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
+          float *Y, int batch, void *stream);
+
+/* Bytes of caller-owned device workspace moe_ffn needs for these sizes
+ * (f64 router logits, the k routes, the k SwiGLU activations).  Returns 0
+ * for invalid sizes. */
+size_t moe_ffn_workspace_bytes(int64_t n_experts, int64_t top_k,
+                               int64_t expert_dim);
+
+/*
+ * moe_ffn: one token through a Qwen3-MoE-style routed-expert FFN
+ * (forward_qwen3_moe_resident.rs, module doc and moe_layer):
+ *
+ *   logits[e] = sum_i router[e][i] * x[i]            router F32 [E][H],
+ *                                                    accumulated in f64
+ *   (sel, w)  = top_k of softmax(logits), renormalised over the k chosen;
+ *               experts ranked by logit (descending), ties to the lower
+ *               index; rank order is also weight order
+ *   for each slot s < k, expert e = sel[s]:
+ *     g = gate[e] x,  u = up[e] x                     [F][H] stacks
+ *     a[s] = w[s] * silu(g) * u,  silu(v) = v / (1 + exp(-v))
+ *   y = residual + sum_s down[e] a[s]                 down: [E][H][F]
+ *
+ *   x, residual   float [H].  y float [H]; y may alias residual (the pages
+ *                 update the hidden state in place); y must not alias x.
+ *   router        float [E][H] (F32 only).
+ *   gate, up      stacks of E matrices [F][H], expert e at
+ *                 base + e * F * qg_row_bytes(fmt, H) (ExpertStack::expert);
+ *                 formats gate_fmt / up_fmt, any block format.
+ *   down          stack of E matrices [H][F], format down_fmt.
+ *   hidden H, n_experts E, top_k k, expert_dim F: positive, k <= E,
+ *                 k <= 32, E <= 1024, H and F multiples of the block sizes.
+ *   sel_experts   int32 [k] or NULL: the chosen experts in rank order.
+ *   sel_weights   float [k] or NULL: their renormalised weights.
+ *   workspace     device memory of at least
+ *                 moe_ffn_workspace_bytes(E, k, F) bytes, 16-byte aligned.
+ *                 Its first E doubles hold the router logits after the call.
+ *                 Overwritten by every call; no initial contents needed.
+ *   stream        hipStream_t or NULL.
+ *
+ * Three kernels are enqueued (router; routing + gate/up + SwiGLU; down +
+ * residual).  No host round trip takes place between them.
+ */
+int moe_ffn(const float *x, const float *residual, float *y,
+            const float *router, int gate_fmt, const void *gate, int up_fmt,
+            const void *up, int down_fmt, const void *down, int64_t hidden,
+            int64_t n_experts, int64_t top_k, int64_t expert_dim,
+            int32_t *sel_experts, float *sel_weights, void *workspace,
+            size_t workspace_bytes, void *stream);
+
+/*
+ * qg_route_topk: the routing step of moe_ffn on its own, on given logits
+ * (forward_qwen3_moe_resident.rs module doc: softmax, top-k, renormalise).
+ *
+ *   logits       double [n_experts] (device).
+ *   sel_experts  int32 [top_k], sel_weights float [top_k] (device): the
+ *                chosen experts in rank order and their weights; both
+ *                required.
+ *   n_experts 1..1024, top_k 1..min(32, n_experts).
+ *
+ * One workgroup; the same device code moe_ffn uses, so a test can check the
+ * selection bit for bit on identical logits.
+ */
+int qg_route_topk(const double *logits, int64_t n_experts, int64_t top_k,
+                  int32_t *sel_experts, float *sel_weights, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

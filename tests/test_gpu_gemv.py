@@ -1,0 +1,153 @@
+"""GPU parity of qgemv against the CPU oracle (element by element).
+
+Small shapes span several lane tiles, several row groups and ragged row
+tails; the workload shapes run at their full size in the launch
+configuration the benchmark times, checked on sampled rows (every row for
+the two small ones).  Tolerance: |y - y_ref| <= 1e-4 * sum|w x| + 1e-6 per
+output (NaN agrees with NaN).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import assert_agree
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+import gguf_quant_dequant_amd as q  # noqa: E402
+from gpu_util import run_gemv  # noqa: E402
+
+Q4_0, Q8_0, Q4_K, Q5_K, Q6_K, F32 = q.QG_Q4_0, q.QG_Q8_0, q.QG_Q4_K, q.QG_Q5_K, q.QG_Q6_K, q.QG_F32
+
+
+def _matrix(fmt, rows, cols, seed):
+    g = synth.rng(seed)
+    if fmt == F32:
+        return synth.f32_matrix(g, rows, cols, 1.0)
+    return synth.matrix(g, fmt, rows, cols)
+
+
+def _check(fmt, rows, cols, batch, seed, offset=0, what=""):
+    W = _matrix(fmt, rows, cols, seed)
+    X = synth.activations(synth.rng(seed + 7), batch, cols)
+    Y = run_gemv(fmt, W, rows, cols, X, offset=offset)
+    Yr, A = oracle.gemv(fmt, W, rows, cols, X)
+    assert_agree(Y, Yr, A, what or f"fmt {fmt} {rows}x{cols} b{batch} off{offset}")
+
+
+SMALL = {
+    Q8_0: [(37, 96), (300, 1056), (5, 32)],
+    Q4_0: [(37, 96), (300, 1056), (5, 32)],
+    Q4_K: [(37, 256), (300, 2304), (3, 768)],
+    Q5_K: [(37, 256), (300, 2304), (3, 768)],
+    Q6_K: [(37, 256), (300, 2304), (3, 768)],
+    F32: [(37, 100), (300, 1028), (5, 4)],
+}
+
+
+@pytest.mark.parametrize("fmt", list(SMALL))
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_small_shapes_every_batch(fmt, batch):
+    for i, (rows, cols) in enumerate(SMALL[fmt]):
+        _check(fmt, rows, cols, batch, 1000 + 10 * fmt + i)
+
+
+@pytest.mark.parametrize("fmt", [Q8_0, Q4_0, Q4_K, Q5_K, Q6_K])
+@pytest.mark.parametrize("batch", [1, 4, 8])
+def test_weights_at_two_bytes_past_alignment(fmt, batch):
+    _check(fmt, 41, 1024 if fmt in (Q8_0, Q4_0) else 768, batch, 2000 + fmt, offset=2)
+
+
+@pytest.mark.parametrize("fmt,cols", [
+    (Q4_K, 32768), (Q5_K, 32768), (Q6_K, 32768), (Q8_0, 16384), (Q4_0, 16384), (F32, 16384),
+])
+def test_widest_supported_rows(fmt, cols):
+    # 512 lane tiles per row: eight waves per row group, reduced through LDS
+    _check(fmt, 19, cols, 1, 3000 + fmt)
+
+
+@pytest.mark.parametrize("fmt,cols", [(Q4_K, 16384), (Q4_0, 14336), (Q6_K, 8192)])
+def test_wide_rows_large_batch(fmt, cols):
+    # batch 8 with more tiles than one row group holds: split into batch chunks
+    _check(fmt, 23, cols, 8, 3100 + fmt)
+
+
+@pytest.mark.parametrize("fmt,cols", [(Q4_K, 33024), (Q8_0, 16416), (F32, 16388)])
+def test_too_wide_rows_are_refused(fmt, cols):
+    W = torch.zeros(q.qg_row_bytes(fmt, cols) * 2 + 64, dtype=torch.uint8, device="cuda")
+    X = torch.zeros(cols, device="cuda")
+    Y = torch.zeros(2, device="cuda")
+    with pytest.raises(q.QGError) as e:
+        q.qgemv(fmt, W, 2, cols, X, Y, 1)
+    assert e.value.code == q.QG_EUNSUPPORTED
+
+
+def test_single_row_and_single_block():
+    for fmt, cols in [(Q8_0, 32), (Q4_0, 32), (Q4_K, 256), (Q5_K, 256), (Q6_K, 256)]:
+        _check(fmt, 1, cols, 1, 4000 + fmt)
+
+
+def test_nan_and_inf_scales_propagate():
+    rows, cols = 6, 512
+    W = synth.matrix(synth.rng(5000), Q6_K, rows, cols)
+    W[1, 208:210] = np.frombuffer(np.float16(np.nan).tobytes(), np.uint8)
+    W[3, 210 + 208:210 + 210] = np.frombuffer(np.float16(np.inf).tobytes(), np.uint8)
+    X = synth.activations(synth.rng(5001), 1, cols)
+    Y = run_gemv(Q6_K, W, rows, cols, X)
+    Yr, A = oracle.gemv(Q6_K, W, rows, cols, X)
+    assert np.isnan(Y[0, 1]) and np.isnan(Yr[0, 1])
+    assert_agree(Y, Yr, A, "nan/inf scales")
+
+
+def test_zero_weights_give_zero():
+    for fmt, cols in [(Q8_0, 64), (Q4_K, 512), (Q6_K, 512)]:
+        W = np.zeros((9, q.qg_row_bytes(fmt, cols)), np.uint8)
+        X = synth.activations(synth.rng(6000), 3, cols)
+        Y = run_gemv(fmt, W, 9, cols, X)
+        assert np.array_equal(Y, np.zeros_like(Y))
+
+
+def test_q8_0_code_minus_128():
+    W = synth.matrix(synth.rng(6100), Q8_0, 4, 64)
+    W[:, 2] = 0x80
+    X = synth.activations(synth.rng(6101), 2, 64)
+    Y = run_gemv(Q8_0, W, 4, 64, X)
+    Yr, A = oracle.gemv(Q8_0, W, 4, 64, X)
+    assert_agree(Y, Yr, A, "q8_0 -128")
+
+
+def test_run_to_run_bitwise_identical():
+    W = synth.matrix(synth.rng(7000), Q4_K, 1000, 4096)
+    X = synth.activations(synth.rng(7001), 4, 4096)
+    a = run_gemv(Q4_K, W, 1000, 4096, X)
+    b = run_gemv(Q4_K, W, 1000, 4096, X)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ------------------------------------------------ workload shapes, full size
+
+def _sample_rows(rows, n, seed):
+    g = np.random.default_rng(seed)
+    idx = np.unique(np.concatenate([np.arange(min(64, rows)), np.arange(max(0, rows - 64), rows),
+                                    g.integers(0, rows, n)]))
+    return idx
+
+
+@pytest.mark.parametrize("name", list(synth.GEMV_CASES))
+def test_workload_full_size(name):
+    case = synth.GEMV_CASES[name]
+    for batch in case.batches:
+        W, X = synth.gemv_inputs(case, batch)
+        Y = run_gemv(case.fmt, W, case.rows, case.cols, X)
+        if case.rows * case.cols <= 4096 * 4096:
+            Yr, A = oracle.gemv(case.fmt, W, case.rows, case.cols, X)
+            assert_agree(Y, Yr, A, f"{name} b{batch}")
+        else:
+            idx = _sample_rows(case.rows, 1500, case.seed + batch)
+            Yr, A = oracle.gemv(case.fmt, W, case.rows, case.cols, X, row_idx=idx)
+            assert_agree(Y[:, idx], Yr, A, f"{name} b{batch} (sampled rows)")
+            assert np.isfinite(Y).all()
