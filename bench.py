@@ -1,0 +1,268 @@
+#!/usr/bin/env python3
+"""Benchmark of the gfx950 fused dequantise-and-dot GEMV and MoE FFN.
+
+Prints ONE JSON line.  The headline workload is the Q4_K 4096 x 4096 GEMV at
+batch 1; a step is one qgemv over that matrix.  The other workloads (Q8_0
+256 x 1024, the Q6_K 151936 x 2048 lm_head, the Q5_K / Q4_0 batch sweep and
+the Qwen3-30B-A3B-shaped MoE FFN) are measured in the same run and reported
+under "workloads".
+
+Cold weights: every launch reads a different copy of the weights, and the
+copies together exceed the 256 MB Infinity Cache and the L2s several times
+over, so each launch streams its weights from HBM.  Inputs are resident in
+HBM before the timed region starts.
+
+Timing: the K launches of a workload are captured in one HIP graph (the
+host cannot issue launches as fast as the kernels run).  The timed region
+is one replay of that graph, bracketed by torch.cuda.synchronize(): its wall
+time gives the whole-job rate (`value`), and a HIP event pair recorded on the
+replay stream gives the average launch duration behind `roofline`.
+`cpu_baseline` times the C oracle (single thread) on a bounded sample of the
+same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+COLD_BYTES = 1 << 30       # weight copies per workload cover at least 1 GiB
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=2, help="untimed graph replays")
+    ap.add_argument("--quick", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--moe-tokens", type=int, default=256)
+    ap.add_argument("--only", default="", help="comma list of workload names (profiling)")
+    return ap.parse_args()
+
+
+class Gemv:
+    """A GEMV workload with enough device copies of W to stay cold."""
+
+    def __init__(self, case, batch, torch, q):
+        import synth
+        self.case, self.batch, self.q, self.torch = case, batch, q, torch
+        W, X = synth.gemv_inputs(case, batch)
+        self.wbytes = W.nbytes
+        ncopy = max(2, -(-COLD_BYTES // self.wbytes))
+        first = torch.from_numpy(W.reshape(-1)).cuda()
+        self.copies = [first] + [first.clone() for _ in range(ncopy - 1)]
+        self.X = torch.from_numpy(X).cuda()
+        self.Y = torch.empty(batch, case.rows, device="cuda")
+        self.i = 0
+
+    def launch(self):
+        W = self.copies[self.i % len(self.copies)]
+        self.i += 1
+        self.q.qgemv(self.case.fmt, W, self.case.rows, self.case.cols, self.X, self.Y,
+                     self.batch)
+
+
+class Moe:
+    """The MoE FFN for one token per call; several device copies of the
+    stacked weights (one per emulated layer) keep the expert reads cold."""
+
+    def __init__(self, case, torch, q, tokens):
+        import synth
+        self.case, self.q, self.torch = case, q, torch
+        router, gate, up, down = synth.moe_weights(case)
+        per = router.nbytes + gate.nbytes + up.nbytes + down.nbytes
+        layers = max(2, -(-4 * COLD_BYTES // per))
+        r0 = torch.from_numpy(router).cuda()
+        g0 = torch.from_numpy(gate.reshape(-1)).cuda()
+        u0 = torch.from_numpy(up.reshape(-1)).cuda()
+        d0 = torch.from_numpy(down.reshape(-1)).cuda()
+        self.layers = [(r0, g0, u0, d0)] + [(r0.clone(), g0.clone(), u0.clone(), d0.clone())
+                                            for _ in range(layers - 1)]
+        xs, rs = synth.moe_tokens(case)
+        reps = -(-tokens // xs.shape[0])
+        self.x = torch.from_numpy(np.tile(xs, (reps, 1))[:tokens]).cuda()
+        self.res = torch.from_numpy(np.tile(rs, (reps, 1))[:tokens]).cuda()
+        self.y = torch.empty_like(self.x)
+        self.sel = torch.empty(tokens, case.top_k, dtype=torch.int32, device="cuda")
+        self.w = torch.empty(tokens, case.top_k, device="cuda")
+        self.wsb = q.moe_ffn_workspace_bytes(case.n_experts, case.top_k, case.expert_dim)
+        self.ws = torch.empty(self.wsb, dtype=torch.uint8, device="cuda")
+        self.i = 0
+        self.tokens = tokens
+        # algorithmic bytes per token: router + k experts' gate, up and down
+        c = case
+        rb_g = q.qg_row_bytes(c.gate_fmt, c.hidden)
+        rb_d = q.qg_row_bytes(c.down_fmt, c.expert_dim)
+        self.bytes_per_token = (4 * c.n_experts * c.hidden
+                                + c.top_k * (2 * c.expert_dim * rb_g + c.hidden * rb_d))
+
+    def launch(self):
+        c = self.case
+        t = self.i % self.tokens
+        r, g, u, d = self.layers[self.i % len(self.layers)]
+        self.i += 1
+        self.q.moe_ffn(self.x[t], self.res[t], self.y[t], r, c.gate_fmt, g, c.up_fmt, u,
+                       c.down_fmt, d, c.hidden, c.n_experts, c.top_k, c.expert_dim,
+                       self.sel[t], self.w[t], self.ws, self.wsb)
+
+
+def time_launches(torch, work, steps, warmup):
+    """Capture `steps` back-to-back launches in one HIP graph, replay it
+    `warmup` times untimed, then time one replay: wall clock between two
+    synchronisations and a HIP event pair on the replay stream.  Returns
+    (wall seconds, event milliseconds)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            work.launch()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(steps):
+            work.launch()
+    for _ in range(max(1, warmup)):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return wall, e0.elapsed_time(e1)
+
+
+def cpu_baseline(seconds):
+    """The oracle (single-threaded C) on the headline workload: whole
+    Q4_K 4096 x 4096 GEMVs repeated until `seconds` have passed."""
+    import oracle
+    import synth
+    case = synth.GEMV_CASES["q4_k_4096x4096"]
+    W, X = synth.gemv_inputs(case, 1)
+    oracle.gemv(case.fmt, W[:8], 8, case.cols, X)  # load / warm
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemv(case.fmt, W, case.rows, case.cols, X)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    gbs = n * W.nbytes / el / 1e9
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} full Q4_K 4096x4096 batch-1 GEMVs in {el:.1f} s "
+                      f"(f64 dequantise-and-dot, one thread, {platform.processor() or 'host'})"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
+              "sharding of this path is described, not built", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import gguf_quant_dequant_amd as q
+    import synth
+
+    q.load_library()
+    torch.cuda.set_device(0)
+    only = set(filter(None, args.only.split(",")))
+
+    head_case = synth.GEMV_CASES["q4_k_4096x4096"]
+    results = {}
+    head = None
+    if not only or "q4_k_4096x4096_b1" in only:
+        head = Gemv(head_case, 1, torch, q)
+        wall, ev_ms = time_launches(torch, head, args.steps, args.warmup)
+        per_us = ev_ms * 1e3 / args.steps
+        results["q4_k_4096x4096_b1"] = dict(
+            weight_bytes=head.wbytes, launches=args.steps,
+            wall_gbs=round(args.steps * head.wbytes / wall / 1e9, 1),
+            event_us_per_launch=round(per_us, 3),
+            event_gbs=round(head.wbytes / (per_us * 1e-6) / 1e9, 1))
+        head_wall, head_us = wall, per_us
+        del head
+
+    if not args.quick:
+        sweep = [("q8_0_256x1024", 1), ("q6_k_151936x2048", 1)]
+        sweep += [("q5_k_14336x4096", b) for b in (1, 4, 8)]
+        sweep += [("q4_0_4096x14336", b) for b in (1, 4, 8)]
+        for name, b in sweep:
+            key = f"{name}_b{b}"
+            if only and key not in only:
+                continue
+            case = synth.GEMV_CASES[name]
+            w = Gemv(case, b, torch, q)
+            steps = max(50, min(args.steps, int(4e9 // w.wbytes)))
+            wall, ev_ms = time_launches(torch, w, steps, args.warmup)
+            per_us = ev_ms * 1e3 / steps
+            results[key] = dict(
+                weight_bytes=w.wbytes, launches=steps,
+                wall_gbs=round(steps * w.wbytes / wall / 1e9, 1),
+                event_us_per_launch=round(per_us, 3),
+                event_gbs=round(w.wbytes / (per_us * 1e-6) / 1e9, 1),
+                event_frac_hbm=round(w.wbytes / (per_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 3))
+            del w
+            torch.cuda.empty_cache()
+        if not only or "moe_ffn_qwen3_30b_a3b" in only:
+            m = Moe(synth.MOE_CASE, torch, q, args.moe_tokens)
+            steps = max(64, min(args.steps, 1000))
+            wall, ev_ms = time_launches(torch, m, steps, args.warmup)
+            per_us = ev_ms * 1e3 / steps
+            results["moe_ffn_qwen3_30b_a3b"] = dict(
+                bytes_per_token=m.bytes_per_token, tokens=steps,
+                wall_tokens_per_s=round(steps / wall, 1),
+                event_us_per_token=round(per_us, 3),
+                tokens_per_s=round(1e6 / per_us, 1),
+                effective_gbs=round(m.bytes_per_token / (per_us * 1e-6) / 1e9, 1))
+            del m
+
+    line = {
+        "metric": "quantized GEMV weight GB/s (Q4_K 4096x4096, batch 1)",
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic, seeded (Q4_K fields: d, dmin ~ U[1e-3,1e-2], 6-bit scales and "
+                "nibbles uniform; x ~ N(0,1)); weights cold in HBM",
+        "config": {"workload": "Q4_K GEMV 4096 x 4096, batch 1", "rows": 4096, "cols": 4096,
+                   "batch": 1, "format": "Q4_K", "weight_bytes": head_case.rows * 2304,
+                   "cold_copies": True},
+    }
+    if "q4_k_4096x4096_b1" in results:
+        r = results["q4_k_4096x4096_b1"]
+        wb = r["weight_bytes"]
+        line["value"] = r["wall_gbs"]
+        line["ms_per_step"] = round(head_wall / args.steps * 1e3, 6)
+        achieved = wb / (head_us * 1e-6) / 1e9
+        line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                            "traffic": None,
+                            "kernel": "qgemv_kernel<FmtK45<32,false,false>,1,4>",
+                            "bytes_per_launch": wb}
+    line["workloads"] = results
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -14,6 +14,18 @@
 
 using namespace qg;
 
+// Launch tuning (compile-time): rows per row group per iteration for batch 1
+// and for larger batches, and workgroups per CU in a launch.
+#ifndef QG_U_B1
+#define QG_U_B1 2
+#endif
+#ifndef QG_U_BN
+#define QG_U_BN 2
+#endif
+#ifndef QG_GRID_PER_CU
+#define QG_GRID_PER_CU 8
+#endif
+
 namespace {
 
 thread_local char g_err[512] = "";
@@ -72,7 +84,7 @@ int max_grid() {
             n > 0)
             cus = n;
     }
-    v = cus * 8;
+    v = cus * QG_GRID_PER_CU;
     cached.store(v, std::memory_order_relaxed);
     return v;
 }
@@ -157,7 +169,7 @@ int launch_gemv(GemvParams p, hipStream_t st) {
 
 template <int B>
 int dispatch_gemv_b(int fmt, bool aligned, int cpt, const GemvParams &p, hipStream_t st) {
-    constexpr int U = B == 1 ? 4 : 2;
+    constexpr int U = B == 1 ? QG_U_B1 : QG_U_BN;
     constexpr int K45 = lw_k45(B), Q6 = lw_q6k(B), Q8 = lw_q80(B), Q4 = lw_q40(B);
     constexpr int FM = lw_f32max(B);
     switch (fmt) {

@@ -101,9 +101,6 @@ template <int J>
 __device__ __forceinline__ float sbyte(uint32_t v) {
     return (float)(int8_t)(v >> (8 * J));
 }
-__device__ __forceinline__ int sbyte_rt(uint32_t v, uint32_t j) {
-    return (int)(int8_t)(v >> (8 * j));
-}
 
 // --------------------------------------------------------------- reductions
 
@@ -123,17 +120,39 @@ __device__ __forceinline__ float xor32_f(float v) {
                                                                   __builtin_bit_cast(int, v)));
 }
 
-// Sum over aligned groups of `width` lanes (width a power of two <= 64,
-// uniform across the wave); every lane of a group receives the group sum.
-// The tree is fixed, so results do not depend on scheduling.
-__device__ __forceinline__ float group_sum(float v, int width) {
-    if (width >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
-    if (width >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
-    if (width >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
-    if (width >= 16) v += dpp_f<0x140>(v); // row_mirror
-    if (width >= 32) v += xor16_f(v);
-    if (width >= 64) v += xor32_f(v);
+// Sum over aligned groups of W lanes (W a power of two <= 64); every lane of
+// a group receives the group sum.  The tree is fixed, so results do not
+// depend on scheduling.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+    if constexpr (W >= 2) v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+    if constexpr (W >= 4) v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+    if constexpr (W >= 8) v += dpp_f<0x141>(v);  // row_half_mirror
+    if constexpr (W >= 16) v += dpp_f<0x140>(v); // row_mirror
+    if constexpr (W >= 32) v += xor16_f(v);
+    if constexpr (W >= 64) v += xor32_f(v);
     return v;
+}
+
+template <int W, int N>
+__device__ __forceinline__ void group_sum_all(float (&v)[N]) {
+#pragma unroll
+    for (int i = 0; i < N; i++) v[i] = group_sum<W>(v[i]);
+}
+
+// group_sum over an array with a width known only at run time (uniform
+// across the workgroup): one scalar branch picks the compile-time tree.
+template <int N>
+__device__ __forceinline__ void group_sum_all(float (&v)[N], int width) {
+    switch (width) {
+    case 2: group_sum_all<2>(v); break;
+    case 4: group_sum_all<4>(v); break;
+    case 8: group_sum_all<8>(v); break;
+    case 16: group_sum_all<16>(v); break;
+    case 32: group_sum_all<32>(v); break;
+    case 64: group_sum_all<64>(v); break;
+    default: break;
+    }
 }
 
 __device__ __forceinline__ double shfl_xor_d(double v, int mask) {

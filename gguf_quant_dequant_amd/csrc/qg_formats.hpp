@@ -204,7 +204,10 @@ struct FmtQ6K {
     template <int B>
     __device__ static void dot(const Raw &w, const Lane &L, const float (&x)[B][CPT],
                                const float (&)[B][NSUM], float (&acc)[B]) {
-        // codes re-centred as signed bytes 4*(q-32): ((q << 2) ^ 0x80)
+        // Each code is assembled as the signed byte 4*(q-32): the low four
+        // bits go to bits 2..5 and the two top bits to bits 6..7 with their
+        // upper bit flipped (qh ^ 0xAA once per dword), so that the byte
+        // read as two's complement is 4*q - 128.
         float at[4][NG][B];
 #pragma unroll
         for (int t = 0; t < 4; t++)
@@ -214,17 +217,16 @@ struct FmtQ6K {
                 for (int b = 0; b < B; b++) at[t][g][b] = 0.f;
 #pragma unroll
         for (int k = 0; k < ND; k++) {
-            const uint32_t a = w.a[k], bq = w.b[k], hh = w.h[k];
+            const uint32_t a = w.a[k], bq = w.b[k], hx = w.h[k] ^ 0xAAAAAAAAu;
             uint32_t q[4];
-            q[0] = (a & 0x0F0F0F0Fu) | ((hh << 4) & 0x30303030u);
-            q[1] = (bq & 0x0F0F0F0Fu) | ((hh << 2) & 0x30303030u);
-            q[2] = ((a >> 4) & 0x0F0F0F0Fu) | (hh & 0x30303030u);
-            q[3] = ((bq >> 4) & 0x0F0F0F0Fu) | ((hh >> 2) & 0x30303030u);
+            q[0] = opaque(((a << 2) & 0x3C3C3C3Cu) | ((hx << 6) & 0xC0C0C0C0u));
+            q[1] = opaque(((bq << 2) & 0x3C3C3C3Cu) | ((hx << 4) & 0xC0C0C0C0u));
+            q[2] = opaque(((a >> 2) & 0x3C3C3C3Cu) | ((hx << 2) & 0xC0C0C0C0u));
+            q[3] = opaque(((bq >> 2) & 0x3C3C3C3Cu) | (hx & 0xC0C0C0C0u));
+            const int g = (4 * k) / 16 < NG ? (4 * k) / 16 : 0;
 #pragma unroll
             for (int t = 0; t < 4; t++) {
-                const uint32_t s = opaque((q[t] << 2) ^ 0x80808080u);
-                const float f[4] = {sbyte<0>(s), sbyte<1>(s), sbyte<2>(s), sbyte<3>(s)};
-                const int g = (4 * k) / 16 < NG ? (4 * k) / 16 : 0;
+                const float f[4] = {sbyte<0>(q[t]), sbyte<1>(q[t]), sbyte<2>(q[t]), sbyte<3>(q[t])};
 #pragma unroll
                 for (int j = 0; j < 4; j++)
 #pragma unroll
@@ -232,14 +234,30 @@ struct FmtQ6K {
                         at[t][g][b] = fmaf(f[j], x[b][t * LW + 4 * k + j], at[t][g][b]);
             }
         }
+        // scale of run t, group g: byte 2t + g + l0/16 of sc[8h..8h+7]
         const float d = f16_lo(w.d) * 0.25f;
-        const uint64_t sc8 = ((uint64_t)w.sc[1] << 32) | w.sc[0];
+        const uint32_t s0 = w.sc[0] >> (8 * L.sbyte0), s1 = w.sc[1] >> (8 * L.sbyte0);
+        float sc[4][NG];
+        if constexpr (NG == 1) {
+            sc[0][0] = sbyte<0>(s0);
+            sc[1][0] = sbyte<2>(s0);
+            sc[2][0] = sbyte<0>(s1);
+            sc[3][0] = sbyte<2>(s1);
+        } else {
+            sc[0][0] = sbyte<0>(w.sc[0]);
+            sc[0][1] = sbyte<1>(w.sc[0]);
+            sc[1][0] = sbyte<2>(w.sc[0]);
+            sc[1][1] = sbyte<3>(w.sc[0]);
+            sc[2][0] = sbyte<0>(w.sc[1]);
+            sc[2][1] = sbyte<1>(w.sc[1]);
+            sc[3][0] = sbyte<2>(w.sc[1]);
+            sc[3][1] = sbyte<3>(w.sc[1]);
+        }
 #pragma unroll
         for (int t = 0; t < 4; t++)
 #pragma unroll
             for (int g = 0; g < NG; g++) {
-                const uint32_t idx = (uint32_t)(2 * t + g) + L.sbyte0;
-                const float s = d * (float)(int8_t)(sc8 >> (8 * idx));
+                const float s = d * sc[t][g];
 #pragma unroll
                 for (int b = 0; b < B; b++) acc[b] = fmaf(s, at[t][g][b], acc[b]);
             }

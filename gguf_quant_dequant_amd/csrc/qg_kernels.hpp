@@ -57,6 +57,69 @@ __device__ __forceinline__ rsrc_t rows_rsrc(const uint8_t *W, uint64_t w_bytes, 
 }
 
 template <class F, int B, int U>
+__device__ __forceinline__ void gemv_issue(const GemvParams &p, int64_t it, int grp, bool active,
+                                           const typename F::Lane &L,
+                                           typename F::Raw (&raw)[U]) {
+    const int64_t r0 = it * ((int64_t)p.G * U);
+    uint32_t delta;
+    const rsrc_t rs = rows_rsrc(p.W, p.w_bytes, (uint64_t)r0 * p.row_bytes, &delta);
+    const int64_t rg = r0 + (int64_t)grp * U;
+#pragma unroll
+    for (int u = 0; u < U; u++)
+        if (active && rg + u < p.rows)
+            F::load(rs, delta + (uint32_t)(grp * U + u) * p.row_bytes, L, raw[u]);
+}
+
+// Dequantise-and-dot of one block of rows already loaded into raw, then the
+// reduction across the row group and the stores.
+template <class F, int B, int U>
+__device__ __forceinline__ void gemv_finish(const GemvParams &p, int64_t it, int grp, int lig,
+                                            int lane, int wave, bool active,
+                                            const typename F::Lane &L,
+                                            const typename F::Raw (&raw)[U],
+                                            const float (&x)[B][F::CPT],
+                                            const float (&sx)[B][F::NSUM],
+                                            float (*red)[U * B]) {
+    const int64_t rg = it * ((int64_t)p.G * U) + (int64_t)grp * U;
+    float acc[U * B];
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+        float a[B];
+#pragma unroll
+        for (int b = 0; b < B; b++) a[b] = 0.f;
+        if (active && rg + u < p.rows) F::template dot<B>(raw[u], L, x, sx, a);
+#pragma unroll
+        for (int b = 0; b < B; b++) acc[u * B + b] = a[b];
+    }
+    group_sum_all(acc, p.S == 1 ? p.lpr : 64);
+    if (p.S == 1) {
+        if (lig == 0) {
+#pragma unroll
+            for (int u = 0; u < U; u++)
+                if (rg + u < p.rows)
+#pragma unroll
+                    for (int b = 0; b < B; b++) p.Y[b * p.rows + rg + u] = acc[u * B + b];
+        }
+    } else {
+        if (lane == 0) {
+#pragma unroll
+            for (int i = 0; i < U * B; i++) red[wave][i] = acc[i];
+        }
+        __syncthreads();
+        if (wave % p.S == 0 && lane < U * B) {
+            float s = 0.f;
+            for (int w = 0; w < p.S; w++) s += red[wave + w][lane];
+            const int u = lane / B, b = lane % B;
+            if (rg + u < p.rows) p.Y[b * p.rows + rg + u] = s;
+        }
+        __syncthreads();
+    }
+}
+
+// Row blocks are double-buffered: the loads of the next block are issued
+// before the current one is dequantised, so memory latency overlaps compute.
+// The first block's loads go out before the activations are read.
+template <class F, int B, int U>
 __global__ void __launch_bounds__(512) qgemv_kernel(GemvParams p) {
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     int grp, lig;
@@ -69,6 +132,12 @@ __global__ void __launch_bounds__(512) qgemv_kernel(GemvParams p) {
     }
     const bool active = lig < p.tiles;
     const typename F::Lane L = F::init(active ? lig : 0);
+    const int64_t rpi = (int64_t)p.G * U;
+    const int64_t step = gridDim.x;
+
+    typename F::Raw ra[U], rb[U];
+    int64_t it = blockIdx.x;
+    if (it * rpi < p.rows) gemv_issue<F, B, U>(p, it, grp, active, L, ra);
 
     float x[B][F::CPT], sx[B][F::NSUM];
     {
@@ -77,57 +146,14 @@ __global__ void __launch_bounds__(512) qgemv_kernel(GemvParams p) {
     }
 
     __shared__ float red[8][U * B];
-    const int64_t rpi = (int64_t)p.G * U;
-    for (int64_t it = blockIdx.x; it * rpi < p.rows; it += gridDim.x) {
-        const int64_t r0 = it * rpi;
-        uint32_t delta;
-        const rsrc_t rs = rows_rsrc(p.W, p.w_bytes, (uint64_t)r0 * p.row_bytes, &delta);
-        const int64_t rg = r0 + (int64_t)grp * U;
-
-        typename F::Raw raw[U];
-#pragma unroll
-        for (int u = 0; u < U; u++)
-            if (active && rg + u < p.rows)
-                F::load(rs, delta + (uint32_t)(grp * U + u) * p.row_bytes, L, raw[u]);
-
-        float acc[U][B];
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-#pragma unroll
-            for (int b = 0; b < B; b++) acc[u][b] = 0.f;
-            if (active && rg + u < p.rows) F::template dot<B>(raw[u], L, x, sx, acc[u]);
-        }
-
-        const int width = p.S == 1 ? p.lpr : 64;
-#pragma unroll
-        for (int u = 0; u < U; u++)
-#pragma unroll
-            for (int b = 0; b < B; b++) acc[u][b] = group_sum(acc[u][b], width);
-
-        if (p.S == 1) {
-            if (lig == 0) {
-#pragma unroll
-                for (int u = 0; u < U; u++)
-                    if (rg + u < p.rows)
-#pragma unroll
-                        for (int b = 0; b < B; b++) p.Y[b * p.rows + rg + u] = acc[u][b];
-            }
-        } else {
-            if (lane == 0) {
-#pragma unroll
-                for (int u = 0; u < U; u++)
-#pragma unroll
-                    for (int b = 0; b < B; b++) red[wave][u * B + b] = acc[u][b];
-            }
-            __syncthreads();
-            if (wave % p.S == 0 && lane < U * B) {
-                float s = 0.f;
-                for (int w = 0; w < p.S; w++) s += red[wave + w][lane];
-                const int u = lane / B, b = lane % B;
-                if (rg + u < p.rows) p.Y[b * p.rows + rg + u] = s;
-            }
-            __syncthreads();
-        }
+    while (it * rpi < p.rows) {
+        if ((it + step) * rpi < p.rows) gemv_issue<F, B, U>(p, it + step, grp, active, L, rb);
+        gemv_finish<F, B, U>(p, it, grp, lig, lane, wave, active, L, ra, x, sx, red);
+        it += step;
+        if (it * rpi >= p.rows) break;
+        if ((it + step) * rpi < p.rows) gemv_issue<F, B, U>(p, it + step, grp, active, L, ra);
+        gemv_finish<F, B, U>(p, it, grp, lig, lane, wave, active, L, rb, x, sx, red);
+        it += step;
     }
 }
 
@@ -335,11 +361,19 @@ __global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
                 F::template dot<1>(rawu[u], L, x, sx, au[u]);
             }
         }
-        const int width = p.gu_S == 1 ? p.gu_lpr : 64;
+        {
+            float v[2 * U];
 #pragma unroll
-        for (int u = 0; u < U; u++) {
-            ag[u][0] = group_sum(ag[u][0], width);
-            au[u][0] = group_sum(au[u][0], width);
+            for (int u = 0; u < U; u++) {
+                v[2 * u] = ag[u][0];
+                v[2 * u + 1] = au[u][0];
+            }
+            group_sum_all(v, p.gu_S == 1 ? p.gu_lpr : 64);
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                ag[u][0] = v[2 * u];
+                au[u][0] = v[2 * u + 1];
+            }
         }
         if (p.gu_S == 1) {
             if (lig == 0) {
@@ -419,9 +453,14 @@ __global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
             acc[u][0] = 0.f;
             if (active && r0 + u < p.H) F::template dot<1>(raw[u], L, x, sx, acc[u]);
         }
-        const int width = p.dn_S == 1 ? p.dn_lpr : 64;
+        {
+            float v[U];
 #pragma unroll
-        for (int u = 0; u < U; u++) acc[u][0] = group_sum(acc[u][0], width);
+            for (int u = 0; u < U; u++) v[u] = acc[u][0];
+            group_sum_all(v, p.dn_S == 1 ? p.dn_lpr : 64);
+#pragma unroll
+            for (int u = 0; u < U; u++) acc[u][0] = v[u];
+        }
         if (p.dn_S == 1) {
             if (lig == 0) {
 #pragma unroll
