@@ -23,7 +23,15 @@ using namespace qg;
 #define QG_U_BN 2
 #endif
 #ifndef QG_GRID_PER_CU
-#define QG_GRID_PER_CU 8
+#define QG_GRID_PER_CU 4
+#endif
+// 1: GEMV rows are staged through LDS with coalesced 16-byte loads;
+// 0: each lane loads its tile's fields straight from global memory.
+#ifndef QG_STAGE
+#define QG_STAGE 1
+#endif
+#ifndef QG_U_STAGE
+#define QG_U_STAGE 2
 #endif
 
 namespace {
@@ -158,10 +166,22 @@ int launch_gemv(GemvParams p, hipStream_t st) {
     p.lpr = s.lpr;
     p.S = s.S;
     p.G = s.G;
-    const int64_t per_iter = (int64_t)s.G * U;
+    constexpr int US = QG_U_STAGE;
+    // the stage holds kStageChunks 16-byte chunks per thread; the block's
+    // rows plus up to 15 bytes of leading alignment and the realigning
+    // reads' extra dword past the last field must fit
+    const size_t stage_bytes = (size_t)kStageChunks * 16 * s.threads;
+    const bool staged =
+        QG_STAGE && (size_t)s.G * US * p.row_bytes + 15 + 4 <= stage_bytes;
+    const int u_used = staged ? US : U;
+    const int64_t per_iter = (int64_t)s.G * u_used;
     int64_t iters = (p.rows + per_iter - 1) / per_iter;
     const int grid = (int)(iters < max_grid() ? iters : max_grid());
-    hipLaunchKernelGGL((qgemv_kernel<F, B, U>), dim3(grid), dim3(s.threads), 0, st, p);
+    if (staged)
+        hipLaunchKernelGGL((qgemv_lds_kernel<F, B, US>), dim3(grid), dim3(s.threads),
+                           stage_bytes, st, p);
+    else
+        hipLaunchKernelGGL((qgemv_kernel<F, B, U>), dim3(grid), dim3(s.threads), 0, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_ELAUNCH, "qgemv: launch failed: %s", hipGetErrorString(e));
     return QG_OK;

@@ -79,6 +79,54 @@ __device__ __forceinline__ void load_span(rsrc_t r, uint32_t off, uint32_t *out)
     }
 }
 
+// Readers of weight bytes.  The format decoders are written against this
+// interface so the same code reads fields straight from global memory
+// (buffer loads) or from a copy of the rows staged in LDS.
+struct BufReader {
+    rsrc_t r;
+    template <int N>
+    __device__ __forceinline__ void dw(uint32_t off, uint32_t *out) const { load_dw<N>(r, off, out); }
+    template <int N, bool REALIGN>
+    __device__ __forceinline__ void span(uint32_t off, uint32_t *out) const {
+        load_span<N, REALIGN>(r, off, out);
+    }
+    __device__ __forceinline__ uint32_t u16(uint32_t off) const {
+        return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+    }
+};
+
+// Bytes staged in LDS: `base` is 16-byte aligned and byte offsets keep the
+// same value mod 4 as in global memory, so the same realignment applies.
+// Every read is of whole aligned dwords.
+struct LdsReader {
+    const uint32_t *base;
+    template <int N>
+    __device__ __forceinline__ void dw(uint32_t off, uint32_t *out) const {
+        const uint32_t *p = base + (off >> 2);
+#pragma unroll
+        for (int i = 0; i < N; i++) out[i] = p[i];
+    }
+    template <int N, bool REALIGN>
+    __device__ __forceinline__ void span(uint32_t off, uint32_t *out) const {
+        const uint32_t *p = base + (off >> 2);
+        if constexpr (!REALIGN) {
+#pragma unroll
+            for (int i = 0; i < N; i++) out[i] = p[i];
+        } else {
+            uint32_t w[N + 1];
+#pragma unroll
+            for (int i = 0; i <= N; i++) w[i] = p[i];
+            const uint32_t sel = (off & 2u) ? 0x05040302u : 0x03020100u;
+#pragma unroll
+            for (int i = 0; i < N; i++) out[i] = __builtin_amdgcn_perm(w[i + 1], w[i], sel);
+        }
+    }
+    __device__ __forceinline__ uint32_t u16(uint32_t off) const {
+        const uint32_t v = base[off >> 2];
+        return (off & 2u) ? (v >> 16) : (v & 0xFFFFu);
+    }
+};
+
 // A little-endian 16-bit field at a 2-byte-aligned offset.
 __device__ __forceinline__ uint32_t load_u16(rsrc_t r, uint32_t off) {
     return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);

@@ -97,10 +97,11 @@ struct FmtK45 {
         uint32_t q[ND];
         uint32_t qh[FIVE ? ND : 1];
     };
-    __device__ static void load(rsrc_t r, uint32_t row, const Lane &L, Raw &w) {
-        load_span<4, RA>(r, row + L.hoff, w.h);
-        if constexpr (FIVE) load_span<ND, RA>(r, row + L.qhoff, w.qh);
-        load_span<ND, RA>(r, row + L.qoff, w.q);
+    template <class Rd>
+    __device__ static void load(const Rd &r, uint32_t row, const Lane &L, Raw &w) {
+        r.template span<4, RA>(row + L.hoff, w.h);
+        if constexpr (FIVE) r.template span<ND, RA>(row + L.qhoff, w.qh);
+        r.template span<ND, RA>(row + L.qoff, w.q);
     }
 
     template <int B>
@@ -193,12 +194,13 @@ struct FmtQ6K {
         uint32_t sc[2];
         uint32_t d;
     };
-    __device__ static void load(rsrc_t r, uint32_t row, const Lane &L, Raw &w) {
-        load_span<ND, true>(r, row + L.qa, w.a);
-        load_span<ND, true>(r, row + L.qb, w.b);
-        load_span<ND, true>(r, row + L.qh, w.h);
-        load_span<2, true>(r, row + L.sc, w.sc);
-        w.d = load_u16(r, row + L.d);
+    template <class Rd>
+    __device__ static void load(const Rd &r, uint32_t row, const Lane &L, Raw &w) {
+        r.template span<ND, true>(row + L.qa, w.a);
+        r.template span<ND, true>(row + L.qb, w.b);
+        r.template span<ND, true>(row + L.qh, w.h);
+        r.template span<2, true>(row + L.sc, w.sc);
+        w.d = r.u16(row + L.d);
     }
 
     template <int B>
@@ -298,9 +300,10 @@ struct FmtQ80 {
         uint32_t q[ND];
         uint32_t d;
     };
-    __device__ static void load(rsrc_t r, uint32_t row, const Lane &L, Raw &w) {
-        load_span<ND, true>(r, row + L.q, w.q);
-        w.d = load_u16(r, row + L.d);
+    template <class Rd>
+    __device__ static void load(const Rd &r, uint32_t row, const Lane &L, Raw &w) {
+        r.template span<ND, true>(row + L.q, w.q);
+        w.d = r.u16(row + L.d);
     }
 
     template <int B>
@@ -358,9 +361,10 @@ struct FmtQ40 {
         uint32_t q[ND];
         uint32_t d;
     };
-    __device__ static void load(rsrc_t r, uint32_t row, const Lane &L, Raw &w) {
-        load_span<ND, true>(r, row + L.q, w.q);
-        w.d = load_u16(r, row + L.d);
+    template <class Rd>
+    __device__ static void load(const Rd &r, uint32_t row, const Lane &L, Raw &w) {
+        r.template span<ND, true>(row + L.q, w.q);
+        w.d = r.u16(row + L.d);
     }
 
     template <int B>
@@ -420,8 +424,9 @@ struct FmtF32 {
     struct Raw {
         uint32_t v[ND];
     };
-    __device__ static void load(rsrc_t r, uint32_t row, const Lane &L, Raw &w) {
-        load_dw<ND>(r, row + L.off, w.v);
+    template <class Rd>
+    __device__ static void load(const Rd &r, uint32_t row, const Lane &L, Raw &w) {
+        r.template dw<ND>(row + L.off, w.v);
     }
 
     template <int B>

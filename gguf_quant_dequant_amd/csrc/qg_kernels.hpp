@@ -67,7 +67,7 @@ __device__ __forceinline__ void gemv_issue(const GemvParams &p, int64_t it, int 
 #pragma unroll
     for (int u = 0; u < U; u++)
         if (active && rg + u < p.rows)
-            F::load(rs, delta + (uint32_t)(grp * U + u) * p.row_bytes, L, raw[u]);
+            F::load(BufReader{rs}, delta + (uint32_t)(grp * U + u) * p.row_bytes, L, raw[u]);
 }
 
 // Dequantise-and-dot of one block of rows already loaded into raw, then the
@@ -154,6 +154,146 @@ __global__ void __launch_bounds__(512) qgemv_kernel(GemvParams p) {
         if ((it + step) * rpi < p.rows) gemv_issue<F, B, U>(p, it + step, grp, active, L, ra);
         gemv_finish<F, B, U>(p, it, grp, lig, lane, wave, active, L, rb, x, sx, red);
         it += step;
+    }
+}
+
+// ----------------------------------------------------- LDS-staged variant
+//
+// Each iteration a workgroup takes G*U consecutive rows.  Their bytes are
+// read with 16-byte buffer loads in which thread t fetches chunks t,
+// t + nthr, ... of the block (each wave instruction reads one contiguous
+// KiB, every cache line is requested once), held in VGPRs, and written to
+// LDS; after a barrier each lane reads its tile's fields from LDS and
+// proceeds as in qgemv_kernel.  The loads of block i+1 are issued before
+// block i is dequantised, so the copy overlaps the arithmetic.
+//
+// Copies start at the 16-byte boundary at or below the block's first byte.
+// Every thread issues kStageChunks loads per block; a chunk past the array
+// end is out of range (reads zero, no memory access), and the record count
+// is rounded up to 16 bytes, so a chunk that overlaps the array is read
+// whole (its extra bytes lie in the same page).
+
+constexpr int kStageChunks = 8;  // 16-byte chunks per thread per block
+
+struct StageBlock {
+    rsrc_t rs;
+    uint32_t d16;  // offset of the block's first byte in the stage
+    uint32_t nch;  // 16-byte chunks that hold the block
+};
+
+__device__ __forceinline__ StageBlock stage_block(const GemvParams &p, int64_t it, int64_t rpi) {
+    const int64_t r0 = it * rpi;
+    const uint8_t *g0 = p.W + (uint64_t)r0 * p.row_bytes;
+    const uint8_t *g16 = (const uint8_t *)((uintptr_t)g0 & ~(uintptr_t)15);
+    const int64_t nrows = p.rows - r0 < rpi ? p.rows - r0 : rpi;
+    StageBlock b;
+    b.d16 = (uint32_t)(g0 - g16);
+    b.nch = (b.d16 + (uint32_t)nrows * p.row_bytes + 15u) >> 4;
+    const uint64_t rem = (p.w_bytes - (uint64_t)r0 * p.row_bytes + b.d16 + 15) & ~(uint64_t)15;
+    b.rs = make_rsrc(g16, rem > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)rem);
+    return b;
+}
+
+__device__ __forceinline__ void stage_fetch(const StageBlock &b, int tid, uint32_t nthr,
+                                            uint32_t (&reg)[kStageChunks][4]) {
+#pragma unroll
+    for (int j = 0; j < kStageChunks; j++) {
+        // chunks past the block read from an out-of-range offset: zeros,
+        // no memory traffic
+        const uint32_t c = j * nthr + (uint32_t)tid;
+        const uint32_t off = c < b.nch ? 16u * c : 0xFFFFFFF0u;
+        auto v = __builtin_amdgcn_raw_buffer_load_b128(b.rs, off, 0, 0);
+        reg[j][0] = v[0]; reg[j][1] = v[1]; reg[j][2] = v[2]; reg[j][3] = v[3];
+    }
+}
+
+__device__ __forceinline__ void stage_store(uint32_t *stage, int tid, uint32_t nthr,
+                                            const uint32_t (&reg)[kStageChunks][4]) {
+#pragma unroll
+    for (int j = 0; j < kStageChunks; j++) {
+        uint32_t *d = stage + 4 * (j * nthr + (uint32_t)tid);
+        d[0] = reg[j][0]; d[1] = reg[j][1]; d[2] = reg[j][2]; d[3] = reg[j][3];
+    }
+}
+
+template <class F, int B, int U>
+__global__ void __launch_bounds__(512) qgemv_lds_kernel(GemvParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t stage[];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int grp, lig;
+    if (p.S == 1) {
+        grp = wave * (64 / p.lpr) + lane / p.lpr;
+        lig = lane & (p.lpr - 1);
+    } else {
+        grp = wave / p.S;
+        lig = (wave % p.S) * 64 + lane;
+    }
+    const bool active = lig < p.tiles;
+    const typename F::Lane L = F::init(active ? lig : 0);
+    const int64_t rpi = (int64_t)p.G * U;
+    const uint32_t nthr = blockDim.x;
+
+    // the first block's loads are in flight while the activations are read
+    int64_t it = blockIdx.x;
+    uint32_t reg[kStageChunks][4];
+    StageBlock cur = stage_block(p, it, rpi);
+    if (it * rpi < p.rows) stage_fetch(cur, tid, nthr, reg);
+
+    float x[B][F::CPT], sx[B][F::NSUM];
+    {
+        const rsrc_t rx = make_rsrc(p.X, 4u * p.cols * (uint32_t)B);
+        load_tile_x<F, B>(rx, p.cols, L, active, x, sx);
+    }
+    __shared__ float red[8][U * B];
+
+    for (; it * rpi < p.rows; it += gridDim.x) {
+        stage_store(stage, tid, nthr, reg);
+        __syncthreads();
+        const uint32_t d16 = cur.d16;
+        if ((it + gridDim.x) * rpi < p.rows) {
+            cur = stage_block(p, it + gridDim.x, rpi);
+            stage_fetch(cur, tid, nthr, reg);
+        }
+
+        const LdsReader rd{stage};
+        const int64_t rg = it * rpi + (int64_t)grp * U;
+        float acc[U * B];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            float a[B];
+#pragma unroll
+            for (int b = 0; b < B; b++) a[b] = 0.f;
+            if (active && rg + u < p.rows) {
+                typename F::Raw raw;
+                F::load(rd, d16 + (uint32_t)(grp * U + u) * p.row_bytes, L, raw);
+                F::template dot<B>(raw, L, x, sx, a);
+            }
+#pragma unroll
+            for (int b = 0; b < B; b++) acc[u * B + b] = a[b];
+        }
+        group_sum_all(acc, p.S == 1 ? p.lpr : 64);
+        if (p.S == 1) {
+            if (lig == 0) {
+#pragma unroll
+                for (int u = 0; u < U; u++)
+                    if (rg + u < p.rows)
+#pragma unroll
+                        for (int b = 0; b < B; b++) p.Y[b * p.rows + rg + u] = acc[u * B + b];
+            }
+        } else {
+            if (lane == 0) {
+#pragma unroll
+                for (int i = 0; i < U * B; i++) red[wave][i] = acc[i];
+            }
+            __syncthreads();
+            if (wave % p.S == 0 && lane < U * B) {
+                float sum = 0.f;
+                for (int w = 0; w < p.S; w++) sum += red[wave + w][lane];
+                const int u = lane / B, b = lane % B;
+                if (rg + u < p.rows) p.Y[b * p.rows + rg + u] = sum;
+            }
+        }
+        __syncthreads();
     }
 }
 
@@ -348,8 +488,8 @@ __global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
             if (active && t < tasks) {
                 const int s = (int)(t / p.F), j = (int)(t % p.F);
                 const uint32_t off = ((uint32_t)s_sel[s] * (uint32_t)p.F + (uint32_t)j) * p.rb_gate;
-                F::load(rg, dg + off, L, rawg[u]);
-                F::load(ru, du + off, L, rawu[u]);
+                F::load(BufReader{rg}, dg + off, L, rawg[u]);
+                F::load(BufReader{ru}, du + off, L, rawu[u]);
             }
         }
         float ag[U][1], au[U][1];
@@ -446,7 +586,7 @@ __global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
 #pragma unroll
         for (int u = 0; u < U; u++)
             if (active && r0 + u < p.H)
-                F::load(rd, dd + expert_off + (uint32_t)(r0 + u) * p.rb_down, L, raw[u]);
+                F::load(BufReader{rd}, dd + expert_off + (uint32_t)(r0 + u) * p.rb_down, L, raw[u]);
         float acc[U][1];
 #pragma unroll
         for (int u = 0; u < U; u++) {
