@@ -256,7 +256,7 @@ def main():
         line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                             "traffic": None,
-                            "kernel": "qgemv_kernel, Q4_K, 64-column lane tiles, batch 1",
+                            "kernel": "qgemv_lds_kernel, Q4_K, 64-column lane tiles, batch 1",
                             "bytes_per_launch": wb}
     line["workloads"] = results
     if not args.no_cpu:

@@ -11,6 +11,7 @@
 
 #include "../../include/qgemv.h"
 #include "qg_kernels.hpp"
+#include "qg_mfma.hpp"
 
 using namespace qg;
 
@@ -32,6 +33,12 @@ using namespace qg;
 #endif
 #ifndef QG_U_STAGE
 #define QG_U_STAGE 2
+#endif
+// Block formats at batch >= QG_MX_MIN_BATCH run on the matrix cores when the
+// activation image and the stage buffers fit in LDS (0 disables).  At batch
+// 1 the VALU kernels are as fast or faster on the measured shapes.
+#ifndef QG_MX_MIN_BATCH
+#define QG_MX_MIN_BATCH 2
 #endif
 
 namespace {
@@ -96,6 +103,8 @@ int max_grid() {
     cached.store(v, std::memory_order_relaxed);
     return v;
 }
+
+bool aligned_to(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
 
 int next_pow2(int v) {
     int p = 1;
@@ -236,6 +245,184 @@ bool tiles_fit(int fmt, int B, int64_t cols) {
     return (cols / cpt) <= 512;
 }
 
+// ------------------------------------------------------- matrix-core GEMV
+
+int device_lds_max() {
+    static std::atomic<int> cached{0};
+    int v = cached.load(std::memory_order_relaxed);
+    if (v) return v;
+    int dev = 0, n = 65536;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        int m = 0;
+        if (hipDeviceGetAttribute(&m, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) ==
+                hipSuccess && m > 0)
+            n = m;
+    }
+    cached.store(n, std::memory_order_relaxed);
+    return n;
+}
+
+int device_cus() { return max_grid() / QG_GRID_PER_CU; }
+
+struct MxPlan {
+    mx::MxParams p;
+    size_t lds;
+    int grid;
+    int tld;
+    bool ra, row16;
+};
+
+// Stage shape for the matrix-core kernel.  When every tile has a workgroup
+// of its own, a workgroup takes its whole tile (up to 16 chunks) in one
+// stage.  Otherwise workgroups stream phases of up to 4 chunks (each chunk
+// split between two waves) through two buffers, sized so that two
+// workgroups share a CU where the activation image allows.
+template <class F, int B>
+bool mx_plan(const void *W, int64_t rows, int64_t cols, int batch, int64_t rb, MxPlan *pl) {
+    constexpr int REC = mx::ximg_rec(B), NB = mx::nb_of(B);
+    const bool row16 = rb % 16 == 0 && F::CHUNK % 16 == 0;
+    const bool ra = F::CHUNK % 4 != 0 || !(row16 && aligned_to(W, 16));
+    const int64_t nc = (cols + mx::kChunk - 1) / mx::kChunk;
+    const int64_t tiles = (rows + mx::kRows - 1) / mx::kRows;
+    const size_t lds_max = (size_t)device_lds_max();
+    const size_t ximg = (size_t)nc * REC, red = (size_t)mx::kWaves * 64 * NB * 4;
+    const size_t out_tile = (size_t)B * mx::kRows * 4;
+    const int cus = device_cus();
+    auto seg_units = [&](int P) { return (P * F::CHUNK + (row16 && !ra ? 0 : 14) + 15) / 16; };
+    auto slot_of = [&](int nu) { return 16 * (nu | 1); };
+
+    int P = 0, npart = 1, nbuf = 1, nu = 0, tld = 16;
+    int64_t grid = 0;
+    size_t stage = 0, lds = 0;
+    if (nc <= 16 && tiles <= 2 * cus) {
+        P = (int)nc;
+        npart = nc >= 8 ? 1 : 2;
+        nu = seg_units(P);
+        stage = (size_t)mx::kRows * slot_of(nu);
+        lds = ximg + stage + red + out_tile;
+        grid = tiles;
+        if (lds > lds_max || mx::kRows * nu > 512 * 16) P = 0;
+    }
+    if (P == 0) {
+        nbuf = 2;
+        tld = 8;
+        npart = 2;
+        for (int per_cu = 2; per_cu >= 1 && P == 0; per_cu--) {
+            for (int Pm = nc < 4 ? (int)nc : 4; Pm >= 1; Pm >>= 1) {
+                nu = seg_units(Pm);
+                stage = (size_t)mx::kRows * slot_of(nu);
+                grid = (int64_t)cus * per_cu;
+                if (grid > tiles) grid = tiles;
+                const size_t out = (size_t)((tiles + grid - 1) / grid) * out_tile;
+                lds = ximg + 2 * stage + red + out;
+                if (lds * per_cu <= lds_max && mx::kRows * nu <= 512 * 8) {
+                    P = Pm;
+                    break;
+                }
+            }
+        }
+        if (P == 0) return false;
+    }
+    mx::MxParams &p = pl->p;
+    p = mx::MxParams{};
+    p.W = (const uint8_t *)W;
+    p.rows = rows;
+    p.w_bytes = (uint64_t)rows * (uint64_t)rb;
+    p.tiles = tiles;
+    p.row_bytes = (uint32_t)rb;
+    p.cols = (uint32_t)cols;
+    p.ximg_bytes = (uint32_t)ximg;
+    p.slot = (uint32_t)slot_of(nu);
+    p.stage_bytes = (uint32_t)stage;
+    p.out_off = (uint32_t)(ximg + nbuf * stage + red);
+    p.batch = batch;
+    p.nc = (int32_t)nc;
+    p.P = P;
+    p.nph = (int32_t)((nc + P - 1) / P);
+    p.npart = npart;
+    p.nu = nu;
+    p.nbuf = nbuf;
+    p.last_nblk = (int32_t)(((cols - 1) % mx::kChunk) / 32 + 1);
+    p.coff = -F::OFF * 0x1p-24f;
+    pl->lds = lds;
+    pl->ra = ra;
+    pl->row16 = row16;
+    pl->grid = (int)grid;
+    // 16-byte loads per thread and stage: the smallest instantiated count
+    const int units = mx::kRows * nu;
+    pl->tld = units <= 512 * 4 ? 4 : (units <= 512 * 8 ? 8 : 16);
+    (void)tld;
+    return true;
+}
+
+template <class F, int B, bool RA, bool ROW16, int TLD>
+int launch_mx(const MxPlan &pl, hipStream_t st) {
+    auto kern = mx::qgemv_mx_kernel<F, B, RA, ROW16, TLD>;
+    static std::atomic<bool> attr{false};
+    if (pl.lds > 65536 && !attr.load(std::memory_order_relaxed)) {
+        (void)hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                  device_lds_max());
+        (void)hipGetLastError();
+        attr.store(true, std::memory_order_relaxed);
+    }
+    hipLaunchKernelGGL(kern, dim3(pl.grid), dim3(512), pl.lds, st, pl.p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_ELAUNCH, "qgemv: launch failed: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+template <class F, int B, bool RA, bool ROW16>
+int launch_mx_t(const MxPlan &pl, hipStream_t st) {
+    switch (pl.tld) {
+    case 4: return launch_mx<F, B, RA, ROW16, 4>(pl, st);
+    case 8: return launch_mx<F, B, RA, ROW16, 8>(pl, st);
+    default: return launch_mx<F, B, RA, ROW16, 16>(pl, st);
+    }
+}
+
+// Runs the matrix-core kernel when the shape fits; *done = false otherwise.
+template <class F, int B>
+int try_mx_f(const void *W, int64_t rows, int64_t cols, const float *X, float *Y, int batch,
+             int64_t rb, hipStream_t st, bool *done) {
+    MxPlan pl;
+    *done = false;
+    if (!mx_plan<F, B>(W, rows, cols, batch, rb, &pl)) return QG_OK;
+    pl.p.X = X;
+    pl.p.Y = Y;
+    *done = true;
+    if constexpr (F::CHUNK % 4 != 0) return launch_mx_t<F, B, true, false>(pl, st);
+    else {
+        if (!pl.ra) return launch_mx_t<F, B, false, true>(pl, st);
+        return launch_mx_t<F, B, true, false>(pl, st);
+    }
+}
+
+template <int B>
+int try_mx_b(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
+             int batch, int64_t rb, hipStream_t st, bool *done) {
+    switch (fmt) {
+    case QG_Q4_K: return try_mx_f<mx::MK45<false>, B>(W, rows, cols, X, Y, batch, rb, st, done);
+    case QG_Q5_K: return try_mx_f<mx::MK45<true>, B>(W, rows, cols, X, Y, batch, rb, st, done);
+    case QG_Q6_K: return try_mx_f<mx::MQ6K, B>(W, rows, cols, X, Y, batch, rb, st, done);
+    case QG_Q8_0: return try_mx_f<mx::MQ80, B>(W, rows, cols, X, Y, batch, rb, st, done);
+    case QG_Q4_0: return try_mx_f<mx::MQ40, B>(W, rows, cols, X, Y, batch, rb, st, done);
+    default: *done = false; return QG_OK;
+    }
+}
+
+int try_mx(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
+           int batch, int64_t rb, hipStream_t st, bool *done) {
+    *done = false;
+    if (QG_MX_MIN_BATCH == 0 || fmt == QG_F32) return QG_OK;
+    // below the threshold only rows too wide for the VALU kernels go here
+    if (batch < QG_MX_MIN_BATCH && tiles_fit(fmt, batch, cols)) return QG_OK;
+    if (batch == 1) return try_mx_b<1>(fmt, W, rows, cols, X, Y, batch, rb, st, done);
+    if (batch <= 2) return try_mx_b<2>(fmt, W, rows, cols, X, Y, batch, rb, st, done);
+    if (batch <= 4) return try_mx_b<4>(fmt, W, rows, cols, X, Y, batch, rb, st, done);
+    return try_mx_b<8>(fmt, W, rows, cols, X, Y, batch, rb, st, done);
+}
+
+
 // ------------------------------------------------------------------- MoE
 
 size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
@@ -329,8 +516,6 @@ int dispatch_down(int fmt, const MoeParams &p, hipStream_t st) {
     }
 }
 
-bool aligned_to(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
-
 }  // namespace
 
 // ========================================================================= ABI
@@ -370,6 +555,10 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
     if (fmt == QG_F32 && cols % 4 != 0)
         return fail(QG_EUNSUPPORTED, "qgemv: F32 rows must be a multiple of 4 floats");
     const int64_t rb = qg_row_bytes(fmt, cols);
+    hipStream_t st = (hipStream_t)stream;
+    bool done = false;
+    const int mrc = try_mx(fmt, W, rows, cols, X, Y, batch, rb, st, &done);
+    if (done) return mrc == QG_OK ? ok() : mrc;
     // Batches too wide for VGPR-resident activations run as several narrower
     // launches over column slices of X and Y.
     int chunk = batch;
@@ -378,7 +567,6 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
         return fail(QG_EUNSUPPORTED, "qgemv: %lld columns of %s exceed the kernel's row width",
                     (long long)cols, fmt_name(fmt));
     const bool aligned = aligned_to(W, 4) && rb % 4 == 0;
-    hipStream_t st = (hipStream_t)stream;
     for (int b0 = 0; b0 < batch; b0 += chunk) {
         const int nb = batch - b0 < chunk ? batch - b0 : chunk;
         GemvParams p{};

@@ -70,14 +70,23 @@ def test_widest_supported_rows(fmt, cols):
     _check(fmt, 19, cols, 1, 3000 + fmt)
 
 
+@pytest.mark.parametrize("fmt", [Q8_0, Q4_0])
+def test_rows_past_the_lane_tile_limit_at_batch_1(fmt):
+    # 513 blocks of 32: more than 512 lane tiles, within the matrix-core
+    # kernel's activation image; the row's last chunk holds one block
+    _check(fmt, 45, 16416, 1, 3200 + fmt)
+
+
 @pytest.mark.parametrize("fmt,cols", [(Q4_K, 16384), (Q4_0, 14336), (Q6_K, 8192)])
 def test_wide_rows_large_batch(fmt, cols):
     # batch 8 with more tiles than one row group holds: split into batch chunks
     _check(fmt, 23, cols, 8, 3100 + fmt)
 
 
-@pytest.mark.parametrize("fmt,cols", [(Q4_K, 33024), (Q8_0, 16416), (F32, 16388)])
+@pytest.mark.parametrize("fmt,cols", [(Q4_K, 33024), (Q8_0, 65536), (F32, 16388)])
 def test_too_wide_rows_are_refused(fmt, cols):
+    # wider than both the matrix-core kernel's LDS activation image and the
+    # VALU kernel's 512 lane tiles per row
     W = torch.zeros(q.qg_row_bytes(fmt, cols) * 2 + 64, dtype=torch.uint8, device="cuda")
     X = torch.zeros(cols, device="cuda")
     Y = torch.zeros(2, device="cuda")
