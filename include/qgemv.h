@@ -105,8 +105,15 @@ const char *qg_last_error(void);
  *   stream hipStream_t or NULL.
  *
  * Dequantisation per element follows the block layouts of the gpu.rs page
- * kernels; products are accumulated in f32 and reduced across lanes with a
- * fixed tree.  Limits: rows < 2^31, cols <= 65536.
+ * kernels.  At batch 1 products are formed and accumulated in f32 on the
+ * vector ALUs and reduced across lanes with a fixed tree.  At batch >= 2
+ * (and for batch-1 rows wider than 512 lane tiles) the block formats run
+ * on the matrix cores: codes are exact f16 values, each 256-column chunk of
+ * X is split into f16 hi + lo parts after a power-of-two scaling (relative
+ * error < 2^-21 per element), sums are f32.  Results are deterministic run
+ * to run.  Limits: rows < 2^31, cols <= 65536; rows that fit neither
+ * kernel (e.g. more than ~64 chunks of 256 columns at batch 1 beyond 512
+ * lane tiles) return QG_EUNSUPPORTED.  Allocates nothing.
  */
 int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
           float *Y, int batch, void *stream);
