@@ -157,6 +157,14 @@ __device__ __forceinline__ float dpp_f(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
                                                               0xF, 0xF, true));
 }
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ uint32_t swz16_u(uint32_t v) {
+    // ds_swizzle bit mode: and 0x1F, or 0, xor 0x10 (within 32-lane halves)
+    return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+}
 __device__ __forceinline__ float xor16_f(float v) {
     // ds_swizzle bit mode: and 0x1F, or 0, xor 0x10 (within 32-lane halves)
     return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v),

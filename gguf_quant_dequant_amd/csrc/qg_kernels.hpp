@@ -357,15 +357,28 @@ __device__ void route_topk_wave(const double *__restrict__ logits, int E, int k,
             bl = take ? kl[i] : bl;
             bi = take ? e : bi;
         }
-#pragma unroll
-        for (int m = 1; m < 64; m <<= 1) {
-            const uint32_t oh = (uint32_t)shfl_xor_i((int)bh, m);
-            const uint32_t ol = (uint32_t)shfl_xor_i((int)bl, m);
-            const int oi = shfl_xor_i(bi, m);
+        // best over the wave: DPP within rows of 16, a swizzle across the
+        // two rows of each half, then the two halves through readlane
+        auto take_best = [&](uint32_t oh, uint32_t ol, int oi) {
             const bool take = key_before(oh, ol, oi, bh, bl, bi);
             bh = take ? oh : bh;
             bl = take ? ol : bl;
             bi = take ? oi : bi;
+        };
+        take_best(dpp_u<0xB1>(bh), dpp_u<0xB1>(bl), (int)dpp_u<0xB1>((uint32_t)bi));
+        take_best(dpp_u<0x4E>(bh), dpp_u<0x4E>(bl), (int)dpp_u<0x4E>((uint32_t)bi));
+        take_best(dpp_u<0x141>(bh), dpp_u<0x141>(bl), (int)dpp_u<0x141>((uint32_t)bi));
+        take_best(dpp_u<0x140>(bh), dpp_u<0x140>(bl), (int)dpp_u<0x140>((uint32_t)bi));
+        take_best(swz16_u(bh), swz16_u(bl), (int)swz16_u((uint32_t)bi));
+        {
+            const uint32_t h0 = __builtin_amdgcn_readlane(bh, 0), l0 = __builtin_amdgcn_readlane(bl, 0);
+            const int i0 = __builtin_amdgcn_readlane(bi, 0);
+            const uint32_t h1 = __builtin_amdgcn_readlane(bh, 32), l1 = __builtin_amdgcn_readlane(bl, 32);
+            const int i1 = __builtin_amdgcn_readlane(bi, 32);
+            const bool t = key_before(h1, l1, i1, h0, l0, i0);
+            bh = t ? h1 : h0;
+            bl = t ? l1 : l0;
+            bi = t ? i1 : i0;
         }
         const uint32_t mine = (lane == (bi & 63)) ? (1u << ((bi >> 6) & 31)) : 0u;
         avail &= ~mine;
@@ -402,16 +415,22 @@ __global__ void __launch_bounds__(64) moe_router_kernel(const float *__restrict_
     const rsrc_t rr = make_rsrc(R + (int64_t)e * H, 4u * (uint32_t)H);
     const rsrc_t rx = make_rsrc(x, 4u * (uint32_t)H);
     double acc = 0.0;
-    // uniform trip count: columns past H read as zero through the resources
-    for (int c0 = 0; c0 < H; c0 += 256) {
-        const int c = c0 + 4 * lane;
-        uint32_t a[4], b[4];
-        load_dw<4>(rr, 4u * c, a);
-        load_dw<4>(rx, 4u * c, b);
+    // 2048 columns per round, all loads of a round issued before its FMAs;
+    // columns past H read as zero through the resources
+    for (int c0 = 0; c0 < H; c0 += 2048) {
+        uint32_t a[8][4], b[8][4];
 #pragma unroll
-        for (int j = 0; j < 4; j++)
-            acc = fma((double)__builtin_bit_cast(float, a[j]),
-                      (double)__builtin_bit_cast(float, b[j]), acc);
+        for (int i = 0; i < 8; i++) {
+            const int c = c0 + 256 * i + 4 * lane;
+            load_dw<4>(rr, 4u * c, a[i]);
+            load_dw<4>(rx, 4u * c, b[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++)
+                acc = fma((double)__builtin_bit_cast(float, a[i][j]),
+                          (double)__builtin_bit_cast(float, b[i][j]), acc);
     }
     acc = wave_sum_d(acc);
     if (lane == 0) logits[e] = acc;
