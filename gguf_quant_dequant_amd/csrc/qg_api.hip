@@ -26,6 +26,13 @@ using namespace qg;
 #ifndef QG_GRID_PER_CU
 #define QG_GRID_PER_CU 4
 #endif
+// The staged GEMV copies the activations through LDS when they take one
+// round of the stage's size, or up to this many when each workgroup stages
+// at most two row blocks; otherwise each lane loads its tile of X from
+// global memory.
+#ifndef QG_XL_ROUNDS
+#define QG_XL_ROUNDS 4
+#endif
 // 1: GEMV rows are staged through LDS with coalesced 16-byte loads;
 // 0: each lane loads its tile's fields straight from global memory.
 #ifndef QG_STAGE
@@ -186,8 +193,18 @@ int launch_gemv(GemvParams p, hipStream_t st) {
     const int64_t per_iter = (int64_t)s.G * u_used;
     int64_t iters = (p.rows + per_iter - 1) / per_iter;
     const int grid = (int)(iters < max_grid() ? iters : max_grid());
-    if (staged)
-        hipLaunchKernelGGL((qgemv_lds_kernel<F, B, US>), dim3(grid), dim3(s.threads),
+    // Activations through LDS when they fit one round of the stage's size,
+    // or a few rounds in a workgroup that stages few row blocks: each further
+    // round adds a load latency to the workgroup's start, which many blocks
+    // amortise less well than the per-lane loads' uncoalesced reads.
+    const int64_t xrounds = ((int64_t)B * p.cols + 32 * s.threads - 1) / (32 * s.threads);
+    const int64_t blocks_per_wg = (iters + grid - 1) / grid;
+    const bool xl = xrounds <= 1 || (xrounds <= QG_XL_ROUNDS && blocks_per_wg <= 2);
+    if (staged && xl)
+        hipLaunchKernelGGL((qgemv_lds_kernel<F, B, US, true>), dim3(grid), dim3(s.threads),
+                           stage_bytes, st, p);
+    else if (staged)
+        hipLaunchKernelGGL((qgemv_lds_kernel<F, B, US, false>), dim3(grid), dim3(s.threads),
                            stage_bytes, st, p);
     else
         hipLaunchKernelGGL((qgemv_kernel<F, B, U>), dim3(grid), dim3(s.threads), 0, st, p);

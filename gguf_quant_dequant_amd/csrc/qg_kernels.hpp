@@ -216,7 +216,87 @@ __device__ __forceinline__ void stage_store(uint32_t *stage, int tid, uint32_t n
     }
 }
 
-template <class F, int B, int U>
+// Activations through LDS.  Loading a lane's tile straight from global
+// memory makes every load instruction touch one cache line per lane (the
+// tiles of neighbouring lanes lie CPT floats apart), which costs more than
+// the weight stream on small matrices.  Instead the workgroup copies
+// X[b][c0, c0 + n) into the stage buffer with coalesced 16-byte loads and
+// each lane then reads its runs from LDS.  16-byte chunk j of a round is
+// stored at chunk j ^ ((j >> 4) & 15): the lanes of one LDS read phase then
+// fall on distinct banks for every tile layout used here (at most two-way
+// conflicts).  X is copied as one flat array of B * cols floats, in rounds
+// of up to 32 floats per thread (the stage's size, a multiple of 2048).
+// Every run of a tile starts at a multiple of RUNLEN, and RUNLEN divides
+// both cols and the round size, so no run straddles two rounds.
+
+__device__ __forceinline__ uint32_t xs_pos(uint32_t j) { return j ^ ((j >> 4) & 15u); }
+
+// Loads 16-byte chunks tid, tid + nthr, ... of a round that starts at byte
+// `off` of X and holds n4 chunks; chunks past n4 read from an out-of-range
+// offset (zeros, no memory access).
+__device__ __forceinline__ void xs_fetch(rsrc_t rx, uint32_t off, uint32_t n4, int tid,
+                                         uint32_t nthr, uint32_t (&reg)[kStageChunks][4]) {
+#pragma unroll
+    for (int j = 0; j < kStageChunks; j++) {
+        const uint32_t c = j * nthr + (uint32_t)tid;
+        const uint32_t o = c < n4 ? off + 16u * c : 0xFFFFFFF0u;
+        auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
+        reg[j][0] = v[0]; reg[j][1] = v[1]; reg[j][2] = v[2]; reg[j][3] = v[3];
+    }
+}
+
+// Every chunk is written, zeros past the round included: xs_pos permutes
+// chunks inside aligned groups of 16 and the stage holds 8 * nthr chunks, a
+// multiple of 16, so all writes stay inside the stage.  (Stores under a
+// predicate would let the compiler sink the loads behind the weight loads.)
+__device__ __forceinline__ void xs_commit(uint32_t *stage, int tid, uint32_t nthr,
+                                          const uint32_t (&reg)[kStageChunks][4]) {
+#pragma unroll
+    for (int j = 0; j < kStageChunks; j++) {
+        uint32_t *d = stage + 4 * xs_pos(j * nthr + (uint32_t)tid);
+        d[0] = reg[j][0]; d[1] = reg[j][1]; d[2] = reg[j][2]; d[3] = reg[j][3];
+    }
+}
+
+// Copies the runs of this lane's tile that lie in floats [f0, f0 + n) of
+// X, taken as one flat array of B rows of `cols` floats, into x.
+template <class F, int B>
+__device__ __forceinline__ void xs_read(const uint32_t *stage, uint32_t f0, uint32_t n,
+                                        uint32_t cols, const typename F::Lane &L, bool active,
+                                        float (&x)[B][F::CPT]) {
+#pragma unroll
+    for (int b = 0; b < B; b++)
+#pragma unroll
+        for (int r = 0; r < F::NRUN; r++) {
+            const uint32_t rel = (uint32_t)b * cols + (uint32_t)F::col0(L, r) - f0;
+            if (active && rel < n) {
+#pragma unroll
+                for (int k = 0; k < F::RUNLEN / 4; k++) {
+                    const uint32_t *q = stage + 4 * xs_pos(rel / 4 + k);
+#pragma unroll
+                    for (int i = 0; i < 4; i++)
+                        x[b][r * F::RUNLEN + 4 * k + i] = __builtin_bit_cast(float, q[i]);
+                }
+            }
+        }
+}
+
+template <class F, int B>
+__device__ __forceinline__ void tile_sums(const float (&x)[B][F::CPT], float (&sx)[B][F::NSUM]) {
+#pragma unroll
+    for (int b = 0; b < B; b++)
+#pragma unroll
+        for (int s = 0; s < F::NSUM; s++) {
+            float a = 0.f;
+            if constexpr (F::NEEDS_SUM) {
+#pragma unroll
+                for (int j = 0; j < F::RUNLEN; j++) a += x[b][s * F::RUNLEN + j];
+            }
+            sx[b][s] = a;
+        }
+}
+
+template <class F, int B, int U, bool XL>
 __global__ void __launch_bounds__(512) qgemv_lds_kernel(GemvParams p) {
     extern __shared__ __attribute__((aligned(16))) uint32_t stage[];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -233,15 +313,46 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(GemvParams p) {
     const int64_t rpi = (int64_t)p.G * U;
     const uint32_t nthr = blockDim.x;
 
-    // the first block's loads are in flight while the activations are read
+    // With XL the first activation round's loads go out first, then the
+    // first block's weight loads (every workgroup has a first block: the
+    // grid is never larger than the number of blocks), so the activations
+    // are staged while the weights are still in flight.  Without XL each
+    // lane reads its tile straight from global memory.
     int64_t it = blockIdx.x;
+    const uint32_t xtot = p.cols * (uint32_t)B;
+    const rsrc_t rx = make_rsrc(p.X, 4u * xtot);
+    const uint32_t xcap = 32u * nthr;  // floats per round: the stage's size
+    uint32_t xr[kStageChunks][4];
+    if constexpr (XL) xs_fetch(rx, 0u, (xtot < xcap ? xtot : xcap) / 4u, tid, nthr, xr);
     uint32_t reg[kStageChunks][4];
     StageBlock cur = stage_block(p, it, rpi);
-    if (it * rpi < p.rows) stage_fetch(cur, tid, nthr, reg);
+    stage_fetch(cur, tid, nthr, reg);
 
     float x[B][F::CPT], sx[B][F::NSUM];
-    {
-        const rsrc_t rx = make_rsrc(p.X, 4u * p.cols * (uint32_t)B);
+    if constexpr (XL) {
+#pragma unroll
+        for (int b = 0; b < B; b++)
+#pragma unroll
+            for (int c = 0; c < F::CPT; c++) x[b][c] = 0.f;
+        {
+            const uint32_t n = xtot < xcap ? xtot : xcap;
+            xs_commit(stage, tid, nthr, xr);
+            __syncthreads();
+            xs_read<F, B>(stage, 0u, n, p.cols, L, active, x);
+        }
+        // further rounds (their loads wait for the weights as well)
+        for (uint32_t f0 = xcap; f0 < xtot; f0 += xcap) {
+            const uint32_t n = xtot - f0 < xcap ? xtot - f0 : xcap;
+            uint32_t yr[kStageChunks][4];
+            __syncthreads();
+            xs_fetch(rx, 4u * f0, n / 4u, tid, nthr, yr);
+            xs_commit(stage, tid, nthr, yr);
+            __syncthreads();
+            xs_read<F, B>(stage, f0, n, p.cols, L, active, x);
+        }
+        tile_sums<F, B>(x, sx);
+        __syncthreads();  // the stage is reused for the weights
+    } else {
         load_tile_x<F, B>(rx, p.cols, L, active, x, sx);
     }
     __shared__ float red[8][U * B];
@@ -329,9 +440,9 @@ __device__ __forceinline__ bool key_before(uint32_t ah, uint32_t al, int ai, uin
 // w_s = exp(l_s - l_0) / sum_{j<k} exp(l_j - l_0), which equals the softmax
 // probabilities renormalised over the chosen set.  Lanes s < k write
 // sel[s], wout[s] (any memory space).
-__device__ void route_topk_wave(const double *__restrict__ logits, int E, int k, int *sel,
-                                float *wout) {
-    constexpr int PER = kMaxExperts / 64;
+template <int PER>
+__device__ void route_topk_per(const double *__restrict__ logits, int E, int k, int *sel,
+                               float *wout) {
     constexpr int NONE = 0x7FFFFFFF;
     const int lane = __lane_id();
     uint32_t kh[PER], kl[PER];
@@ -397,6 +508,23 @@ __device__ void route_topk_wave(const double *__restrict__ logits, int E, int k,
         sel[lane] = chosen_e;
         wout[lane] = (float)(ex / den);
     }
+}
+
+// Each lane holds ceil(E/64) keys, rounded up to a power of two, so the k
+// selection rounds scan only as many slots as the expert count needs.
+__device__ void route_topk_wave(const double *__restrict__ logits, int E, int k, int *sel,
+                                float *wout) {
+    static_assert(kMaxExperts == 64 * 16, "slot dispatch covers up to 16 keys per lane");
+    if (E <= 64)
+        route_topk_per<1>(logits, E, k, sel, wout);
+    else if (E <= 128)
+        route_topk_per<2>(logits, E, k, sel, wout);
+    else if (E <= 256)
+        route_topk_per<4>(logits, E, k, sel, wout);
+    else if (E <= 512)
+        route_topk_per<8>(logits, E, k, sel, wout);
+    else
+        route_topk_per<16>(logits, E, k, sel, wout);
 }
 
 __global__ void __launch_bounds__(64) route_topk_kernel(const double *logits, int E, int k,

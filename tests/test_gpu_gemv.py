@@ -83,6 +83,13 @@ def test_wide_rows_large_batch(fmt, cols):
     _check(fmt, 23, cols, 8, 3100 + fmt)
 
 
+@pytest.mark.parametrize("fmt,cols,batch", [(Q4_0, 14368, 4), (Q8_0, 12320, 3), (Q4_K, 32768, 1)])
+def test_activations_staged_in_several_rounds(fmt, cols, batch):
+    # batch * cols floats exceed one round of the LDS stage (32 floats per
+    # thread); the last round is partial
+    _check(fmt, 9, cols, batch, 3300 + fmt)
+
+
 @pytest.mark.parametrize("fmt,cols", [(Q4_K, 33024), (Q8_0, 65536), (F32, 16388)])
 def test_too_wide_rows_are_refused(fmt, cols):
     # wider than both the matrix-core kernel's LDS activation image and the

@@ -166,6 +166,22 @@ def test_route_random_and_constructed_ties():
         assert np.allclose(w, rw, rtol=1e-6, atol=0)
 
 
+@pytest.mark.parametrize("E", [64, 65, 128, 129, 256, 257, 512, 513, 1024])
+def test_route_key_slot_boundaries(E):
+    # each lane keeps ceil(E/64) keys rounded up to a power of two; the
+    # winners are planted in the last lane and the last slot
+    g = np.random.default_rng(70 + E)
+    lg = g.standard_normal(E)
+    lg[E - 1] = 9.0
+    lg[63] = 8.0
+    lg[E // 2] = 8.0
+    for k in (1, 3, 8):
+        sel, w = _gpu_route(lg, k)
+        rs, rw = oracle.route(lg, k)
+        assert np.array_equal(sel, rs), (E, k)
+        assert np.allclose(w, rw, rtol=1e-6, atol=0)
+
+
 def test_route_nan_logits_rank_last():
     lg = np.array([np.nan, 3.0, np.nan, -1.0, 0.0])
     sel, _ = _gpu_route(lg, 4)
