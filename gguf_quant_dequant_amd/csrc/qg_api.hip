@@ -483,7 +483,8 @@ int launch_gateup(MoeParams p, hipStream_t st) {
     const int64_t tasks = (int64_t)p.K * p.F, per = (int64_t)s.G * U;
     const int64_t iters = (tasks + per - 1) / per;
     const int grid = (int)(iters < max_grid() ? iters : max_grid());
-    hipLaunchKernelGGL((moe_gateup_kernel<F, U>), dim3(grid), dim3(s.threads), 0, st, p);
+    hipLaunchKernelGGL((moe_gateup_kernel<F, U>), dim3(grid), dim3(s.threads),
+                       (size_t)kStageChunks * 16 * s.threads, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(QG_ELAUNCH, "moe_ffn: gate/up launch failed: %s", hipGetErrorString(e));
@@ -504,7 +505,8 @@ int launch_down(MoeParams p, hipStream_t st) {
     const int64_t per = (int64_t)s.G * U;
     const int64_t iters = (p.H + per - 1) / per;
     const int grid = (int)(iters < max_grid() ? iters : max_grid());
-    hipLaunchKernelGGL((moe_down_kernel<F, U>), dim3(grid), dim3(s.threads), 0, st, p);
+    hipLaunchKernelGGL((moe_down_kernel<F, U>), dim3(grid), dim3(s.threads),
+                       (size_t)kStageChunks * 16 * s.threads, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(QG_ELAUNCH, "moe_ffn: down launch failed: %s", hipGetErrorString(e));

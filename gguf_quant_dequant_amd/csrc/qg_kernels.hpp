@@ -259,16 +259,16 @@ __device__ __forceinline__ void xs_commit(uint32_t *stage, int tid, uint32_t nth
 }
 
 // Copies the runs of this lane's tile that lie in floats [f0, f0 + n) of
-// X, taken as one flat array of B rows of `cols` floats, into x.
+// the flat array X into x; tile b starts at float xbase[b] of X.
 template <class F, int B>
 __device__ __forceinline__ void xs_read(const uint32_t *stage, uint32_t f0, uint32_t n,
-                                        uint32_t cols, const typename F::Lane &L, bool active,
-                                        float (&x)[B][F::CPT]) {
+                                        const uint32_t (&xbase)[B], const typename F::Lane &L,
+                                        bool active, float (&x)[B][F::CPT]) {
 #pragma unroll
     for (int b = 0; b < B; b++)
 #pragma unroll
         for (int r = 0; r < F::NRUN; r++) {
-            const uint32_t rel = (uint32_t)b * cols + (uint32_t)F::col0(L, r) - f0;
+            const uint32_t rel = xbase[b] + (uint32_t)F::col0(L, r) - f0;
             if (active && rel < n) {
 #pragma unroll
                 for (int k = 0; k < F::RUNLEN / 4; k++) {
@@ -294,6 +294,38 @@ __device__ __forceinline__ void tile_sums(const float (&x)[B][F::CPT], float (&s
             }
             sx[b][s] = a;
         }
+}
+
+// Stages the xtot floats of X round by round and fills x and sx.  The
+// caller has already issued the first round's loads into xr (so that they
+// can go out ahead of its other loads).  Ends with a barrier: the stage is
+// free again on return.
+template <class F, int B>
+__device__ __forceinline__ void xs_stage(uint32_t *stage, rsrc_t rx, uint32_t xtot,
+                                         const uint32_t (&xbase)[B], const typename F::Lane &L,
+                                         bool active, int tid, uint32_t nthr,
+                                         const uint32_t (&xr)[kStageChunks][4],
+                                         float (&x)[B][F::CPT], float (&sx)[B][F::NSUM]) {
+    const uint32_t xcap = 32u * nthr;
+#pragma unroll
+    for (int b = 0; b < B; b++)
+#pragma unroll
+        for (int c = 0; c < F::CPT; c++) x[b][c] = 0.f;
+    xs_commit(stage, tid, nthr, xr);
+    __syncthreads();
+    xs_read<F, B>(stage, 0u, xtot < xcap ? xtot : xcap, xbase, L, active, x);
+    // further rounds (their loads wait for everything issued before them)
+    for (uint32_t f0 = xcap; f0 < xtot; f0 += xcap) {
+        const uint32_t n = xtot - f0 < xcap ? xtot - f0 : xcap;
+        uint32_t yr[kStageChunks][4];
+        __syncthreads();
+        xs_fetch(rx, 4u * f0, n / 4u, tid, nthr, yr);
+        xs_commit(stage, tid, nthr, yr);
+        __syncthreads();
+        xs_read<F, B>(stage, f0, n, xbase, L, active, x);
+    }
+    tile_sums<F, B>(x, sx);
+    __syncthreads();
 }
 
 template <class F, int B, int U, bool XL>
@@ -330,28 +362,10 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(GemvParams p) {
 
     float x[B][F::CPT], sx[B][F::NSUM];
     if constexpr (XL) {
+        uint32_t xbase[B];
 #pragma unroll
-        for (int b = 0; b < B; b++)
-#pragma unroll
-            for (int c = 0; c < F::CPT; c++) x[b][c] = 0.f;
-        {
-            const uint32_t n = xtot < xcap ? xtot : xcap;
-            xs_commit(stage, tid, nthr, xr);
-            __syncthreads();
-            xs_read<F, B>(stage, 0u, n, p.cols, L, active, x);
-        }
-        // further rounds (their loads wait for the weights as well)
-        for (uint32_t f0 = xcap; f0 < xtot; f0 += xcap) {
-            const uint32_t n = xtot - f0 < xcap ? xtot - f0 : xcap;
-            uint32_t yr[kStageChunks][4];
-            __syncthreads();
-            xs_fetch(rx, 4u * f0, n / 4u, tid, nthr, yr);
-            xs_commit(stage, tid, nthr, yr);
-            __syncthreads();
-            xs_read<F, B>(stage, f0, n, p.cols, L, active, x);
-        }
-        tile_sums<F, B>(x, sx);
-        __syncthreads();  // the stage is reused for the weights
+        for (int b = 0; b < B; b++) xbase[b] = (uint32_t)b * p.cols;
+        xs_stage<F, B>(stage, rx, xtot, xbase, L, active, tid, nthr, xr, x, sx);
     } else {
         load_tile_x<F, B>(rx, p.cols, L, active, x, sx);
     }
@@ -607,13 +621,19 @@ __global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
     }
     const bool active = lig < p.gu_tiles;
     const typename F::Lane L = F::init(active ? lig : 0);
+    // x is staged through LDS (coalesced loads) while wave 0 routes; the
+    // staging's closing barrier also publishes s_sel and s_w
+    extern __shared__ __attribute__((aligned(16))) uint32_t xst[];
+    const uint32_t nthr = blockDim.x, xcap = 32u * nthr, H = (uint32_t)p.H;
+    const rsrc_t rx = make_rsrc(p.x, 4u * H);
+    uint32_t xr[kStageChunks][4];
+    xs_fetch(rx, 0u, (H < xcap ? H : xcap) / 4u, tid, nthr, xr);
+    if (wave == 0) route_topk_wave(p.logits, p.E, p.K, s_sel, s_w);
     float x[1][F::CPT], sx[1][F::NSUM];
     {
-        const rsrc_t rx = make_rsrc(p.x, 4u * (uint32_t)p.H);
-        load_tile_x<F, 1>(rx, (uint32_t)p.H, L, active, x, sx);
+        const uint32_t xbase[1] = {0u};
+        xs_stage<F, 1>(xst, rx, H, xbase, L, active, tid, nthr, xr, x, sx);
     }
-    if (wave == 0) route_topk_wave(p.logits, p.E, p.K, s_sel, s_w);
-    __syncthreads();
     if (blockIdx.x == 0 && tid < p.K) {
         p.ws_sel[tid] = s_sel[tid];
         p.ws_w[tid] = s_w[tid];
@@ -717,13 +737,20 @@ __global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
     const int slot = active ? lig / p.dn_tiles_per_slot : 0;
     const int tile = active ? lig % p.dn_tiles_per_slot : 0;
     const typename F::Lane L = F::init(tile);
-    float x[1][F::CPT], sx[1][F::NSUM];
-    {
-        const rsrc_t ra = make_rsrc(p.act + (int64_t)slot * p.F, 4u * (uint32_t)p.F);
-        load_tile_x<F, 1>(ra, (uint32_t)p.F, L, active, x, sx);
-    }
+    // the activations of all K slots, staged through LDS (coalesced loads)
+    extern __shared__ __attribute__((aligned(16))) uint32_t xst[];
+    const uint32_t nthr = blockDim.x, xcap = 32u * nthr;
+    const uint32_t xtot = (uint32_t)p.K * (uint32_t)p.F;
+    const rsrc_t ra = make_rsrc(p.act, 4u * xtot);
+    uint32_t xr[kStageChunks][4];
+    xs_fetch(ra, 0u, (xtot < xcap ? xtot : xcap) / 4u, tid, nthr, xr);
     const uint32_t expert_off =
         active ? (uint32_t)p.ws_sel[slot] * (uint32_t)p.H * p.rb_down : 0u;
+    float x[1][F::CPT], sx[1][F::NSUM];
+    {
+        const uint32_t xbase[1] = {(uint32_t)slot * (uint32_t)p.F};
+        xs_stage<F, 1>(xst, ra, xtot, xbase, L, active, tid, nthr, xr, x, sx);
+    }
     uint32_t dd;
     const rsrc_t rd = rows_rsrc(p.down, p.down_bytes, 0, &dd);
     const int64_t rpi = (int64_t)p.dn_G * U;
