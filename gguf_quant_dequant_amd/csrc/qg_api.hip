@@ -4,6 +4,9 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <map>
+#include <mutex>
+#include <tuple>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
@@ -16,15 +19,12 @@
 using namespace qg;
 
 // Launch tuning (compile-time): rows per row group per iteration for batch 1
-// and for larger batches, and workgroups per CU in a launch.
+// and for larger batches.
 #ifndef QG_U_B1
 #define QG_U_B1 2
 #endif
 #ifndef QG_U_BN
 #define QG_U_BN 2
-#endif
-#ifndef QG_GRID_PER_CU
-#define QG_GRID_PER_CU 4
 #endif
 // The staged GEMV copies the activations through LDS when they take one
 // round of the stage's size, or up to this many when each workgroup stages
@@ -95,7 +95,7 @@ const char *fmt_name(int fmt) {
 
 // Workgroups per launch: enough to cover every CU several times over; the
 // kernels loop over the rest.
-int max_grid() {
+int device_cus() {
     static std::atomic<int> cached{0};
     int v = cached.load(std::memory_order_relaxed);
     if (v) return v;
@@ -106,9 +106,33 @@ int max_grid() {
             n > 0)
             cus = n;
     }
-    v = cus * QG_GRID_PER_CU;
-    cached.store(v, std::memory_order_relaxed);
-    return v;
+    cached.store(cus, std::memory_order_relaxed);
+    return cus;
+}
+
+// Workgroups of kernel fn (threads, dynamic LDS) that fit on one CU at once,
+// from the occupancy calculator; cached per configuration.
+int resident_per_cu(const void *fn, int threads, size_t lds) {
+    static std::mutex mu;
+    static std::map<std::tuple<const void *, int, size_t>, int> cache;
+    std::lock_guard<std::mutex> g(mu);
+    const auto key = std::make_tuple(fn, threads, lds);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, fn, threads, lds) != hipSuccess || n < 1)
+        n = 1;
+    cache[key] = n;
+    return n;
+}
+
+// A grid-stride kernel's grid: one workgroup per block of work, at most as
+// many as are resident on the whole chip at once, so that no workgroup
+// waits for a slot while others run (every workgroup does about the same
+// work; a second partial round would run at a fraction of the occupancy).
+int resident_grid(const void *fn, int threads, size_t lds, int64_t blocks) {
+    const int64_t cap = (int64_t)device_cus() * resident_per_cu(fn, threads, lds);
+    return (int)(blocks < cap ? blocks : cap);
 }
 
 bool aligned_to(const void *p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
@@ -191,23 +215,29 @@ int launch_gemv(GemvParams p, hipStream_t st) {
         QG_STAGE && (size_t)s.G * US * p.row_bytes + 15 + 4 <= stage_bytes;
     const int u_used = staged ? US : U;
     const int64_t per_iter = (int64_t)s.G * u_used;
-    int64_t iters = (p.rows + per_iter - 1) / per_iter;
-    const int grid = (int)(iters < max_grid() ? iters : max_grid());
+    const int64_t iters = (p.rows + per_iter - 1) / per_iter;
+    const void *k_xl = (const void *)qgemv_lds_kernel<F, B, US, true>;
+    const void *k_st = (const void *)qgemv_lds_kernel<F, B, US, false>;
+    const void *k_direct = (const void *)qgemv_kernel<F, B, U>;
     // Activations through LDS when they fit one round of the stage's size,
     // or a few rounds in a workgroup that stages few row blocks: each further
     // round adds a load latency to the workgroup's start, which many blocks
     // amortise less well than the per-lane loads' uncoalesced reads.
     const int64_t xrounds = ((int64_t)B * p.cols + 32 * s.threads - 1) / (32 * s.threads);
-    const int64_t blocks_per_wg = (iters + grid - 1) / grid;
+    const int grid_xl = resident_grid(k_xl, s.threads, stage_bytes, iters);
+    const int64_t blocks_per_wg = (iters + grid_xl - 1) / grid_xl;
     const bool xl = xrounds <= 1 || (xrounds <= QG_XL_ROUNDS && blocks_per_wg <= 2);
-    if (staged && xl)
-        hipLaunchKernelGGL((qgemv_lds_kernel<F, B, US, true>), dim3(grid), dim3(s.threads),
+    if (staged && xl) {
+        hipLaunchKernelGGL((qgemv_lds_kernel<F, B, US, true>), dim3(grid_xl), dim3(s.threads),
                            stage_bytes, st, p);
-    else if (staged)
+    } else if (staged) {
+        const int grid = resident_grid(k_st, s.threads, stage_bytes, iters);
         hipLaunchKernelGGL((qgemv_lds_kernel<F, B, US, false>), dim3(grid), dim3(s.threads),
                            stage_bytes, st, p);
-    else
+    } else {
+        const int grid = resident_grid(k_direct, s.threads, 0, iters);
         hipLaunchKernelGGL((qgemv_kernel<F, B, U>), dim3(grid), dim3(s.threads), 0, st, p);
+    }
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_ELAUNCH, "qgemv: launch failed: %s", hipGetErrorString(e));
     return QG_OK;
@@ -279,7 +309,7 @@ int device_lds_max() {
     return n;
 }
 
-int device_cus() { return max_grid() / QG_GRID_PER_CU; }
+
 
 struct MxPlan {
     mx::MxParams p;
@@ -482,9 +512,9 @@ int launch_gateup(MoeParams p, hipStream_t st) {
     p.gu_G = s.G;
     const int64_t tasks = (int64_t)p.K * p.F, per = (int64_t)s.G * U;
     const int64_t iters = (tasks + per - 1) / per;
-    const int grid = (int)(iters < max_grid() ? iters : max_grid());
-    hipLaunchKernelGGL((moe_gateup_kernel<F, U>), dim3(grid), dim3(s.threads),
-                       (size_t)kStageChunks * 16 * s.threads, st, p);
+    const size_t lds = (size_t)kStageChunks * 16 * s.threads;
+    const int grid = resident_grid((const void *)moe_gateup_kernel<F, U>, s.threads, lds, iters);
+    hipLaunchKernelGGL((moe_gateup_kernel<F, U>), dim3(grid), dim3(s.threads), lds, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(QG_ELAUNCH, "moe_ffn: gate/up launch failed: %s", hipGetErrorString(e));
@@ -504,9 +534,9 @@ int launch_down(MoeParams p, hipStream_t st) {
     p.dn_G = s.G;
     const int64_t per = (int64_t)s.G * U;
     const int64_t iters = (p.H + per - 1) / per;
-    const int grid = (int)(iters < max_grid() ? iters : max_grid());
-    hipLaunchKernelGGL((moe_down_kernel<F, U>), dim3(grid), dim3(s.threads),
-                       (size_t)kStageChunks * 16 * s.threads, st, p);
+    const size_t lds = (size_t)kStageChunks * 16 * s.threads;
+    const int grid = resident_grid((const void *)moe_down_kernel<F, U>, s.threads, lds, iters);
+    hipLaunchKernelGGL((moe_down_kernel<F, U>), dim3(grid), dim3(s.threads), lds, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(QG_ELAUNCH, "moe_ffn: down launch failed: %s", hipGetErrorString(e));
@@ -517,7 +547,7 @@ int dispatch_gateup(int fmt, const MoeParams &p, hipStream_t st) {
     switch (fmt) {
     case QG_Q4_K: return launch_gateup<FmtQ4K<32, true>>(p, st);
     case QG_Q5_K: return launch_gateup<FmtQ5K<32, true>>(p, st);
-    case QG_Q6_K: return launch_gateup<FmtQ6K<16>>(p, st);
+    case QG_Q6_K: return launch_gateup<FmtQ6K<16, false>>(p, st);
     case QG_Q8_0: return launch_gateup<FmtQ80<32>>(p, st);
     case QG_Q4_0: return launch_gateup<FmtQ40<16>>(p, st);
     default: return fail(QG_EUNSUPPORTED, "moe_ffn: gate/up format %d", fmt);
@@ -528,7 +558,7 @@ int dispatch_down(int fmt, const MoeParams &p, hipStream_t st) {
     switch (fmt) {
     case QG_Q4_K: return launch_down<FmtQ4K<32, true>>(p, st);
     case QG_Q5_K: return launch_down<FmtQ5K<32, true>>(p, st);
-    case QG_Q6_K: return launch_down<FmtQ6K<16>>(p, st);
+    case QG_Q6_K: return launch_down<FmtQ6K<16, false>>(p, st);
     case QG_Q8_0: return launch_down<FmtQ80<32>>(p, st);
     case QG_Q4_0: return launch_down<FmtQ40<16>>(p, st);
     default: return fail(QG_EUNSUPPORTED, "moe_ffn: down format %d", fmt);

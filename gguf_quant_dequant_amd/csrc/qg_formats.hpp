@@ -35,9 +35,92 @@
 // bitwise first), so the only rounding is in the f32 products and sums.
 #pragma once
 
+#include <type_traits>
+
 #include "qg_device.hpp"
 
 namespace qg {
+
+// Activation tile of the f32 decoders: the tile's floats and, for the
+// formats with a min term, per-run sums.
+template <int CPT, int NSUM, int B>
+struct XF32 {
+    float x[B][CPT];
+    float sx[B][NSUM];
+};
+
+template <class F, int B>
+__device__ __forceinline__ void prep_f32(const float (&x)[B][F::CPT],
+                                         XF32<F::CPT, F::NSUM, B> &t) {
+#pragma unroll
+    for (int b = 0; b < B; b++) {
+#pragma unroll
+        for (int c = 0; c < F::CPT; c++) t.x[b][c] = x[b][c];
+#pragma unroll
+        for (int s = 0; s < F::NSUM; s++) {
+            float a = 0.f;
+            if constexpr (F::NEEDS_SUM) {
+#pragma unroll
+                for (int j = 0; j < F::RUNLEN; j++) a += x[b][s * F::RUNLEN + j];
+            }
+            t.sx[b][s] = a;
+        }
+    }
+}
+
+// Activation tile as base-256 digits, for exact integer dot products.
+// Each run of RUNLEN columns gets its own power-of-two scale 2^s, chosen so
+// that the largest |x| * 2^s lies in [2^20, 2^21).  X = x * 2^s, taken to
+// an integer within one unit, is split into digits X = 65536 p2 + 256 p1 +
+// p0 with p0, p1 in [-128, 127] and |p2| <= 33.  Plane k holds digit k of
+// four consecutive columns per dword (column c in byte c % 4), so v_dot4 of
+// four int8 codes with a plane dword is an exact partial sum.  f = 2^-s, or
+// NaN when the run holds a non-finite value.  The rounding of X bounds the
+// error of a product sum by 2^-20 of sum |code| * max|x| over the run.
+template <int CPT, int NRUN, int B>
+struct XI8 {
+    uint32_t p[B][3][CPT / 4];
+    float f[B][NRUN];
+};
+
+template <int RL>
+__device__ __forceinline__ void digits_run(const float *x, uint32_t *p0, uint32_t *p1,
+                                           uint32_t *p2, float *f) {
+    uint32_t mb = 0;
+#pragma unroll
+    for (int j = 0; j < RL; j++) {
+        const uint32_t a = __builtin_bit_cast(uint32_t, x[j]) & 0x7FFFFFFFu;
+        mb = a > mb ? a : mb;
+    }
+    // frexp exponent e: max in [2^(e-1), 2^e); 0 for a zero maximum
+    int s = 21 - __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, mb));
+    s = s > 126 ? 126 : s;
+    const float up = __builtin_bit_cast(float, (uint32_t)(s + 127) << 23);
+    *f = mb < 0x7F800000u ? __builtin_bit_cast(float, (uint32_t)(127 - s) << 23)
+                          : __builtin_nanf("");
+#pragma unroll
+    for (int q = 0; q < RL / 4; q++) {
+        // y = X + 0x8080: bytes 0 and 1 of y are p0 + 128 and p1 + 128,
+        // byte 2 (sign-extended) is p2
+        uint32_t y[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) y[i] = (uint32_t)(int)fmaf(x[4 * q + i], up, 32896.0f);
+        const uint32_t a = __builtin_amdgcn_perm(y[1], y[0], 0x05040100u);
+        const uint32_t b = __builtin_amdgcn_perm(y[3], y[2], 0x05040100u);
+        p0[q] = __builtin_amdgcn_perm(b, a, 0x06040200u) ^ 0x80808080u;
+        p1[q] = __builtin_amdgcn_perm(b, a, 0x07050301u) ^ 0x80808080u;
+        const uint32_t c = __builtin_amdgcn_perm(y[1], y[0], 0x0C0C0602u);
+        const uint32_t e = __builtin_amdgcn_perm(y[3], y[2], 0x0C0C0602u);
+        p2[q] = __builtin_amdgcn_perm(e, c, 0x05040100u);
+    }
+}
+
+// Sum of an exact digit-plane dot product: 65536 s2 + 256 s1 + s0, rounded
+// once to f32.
+__device__ __forceinline__ float digits_sum(int s0, int s1, int s2) {
+    return fmaf((float)((s2 << 8) + s1), 256.0f, (float)s0);
+}
+
 
 // ---------------------------------------------------------------- Q4_K / Q5_K
 //
@@ -104,9 +187,17 @@ struct FmtK45 {
         r.template span<ND, RA>(row + L.qoff, w.q);
     }
 
+    template <int B> using XTile = XF32<CPT, NSUM, B>;
     template <int B>
-    __device__ static void dot(const Raw &w, const Lane &L, const float (&x)[B][CPT],
-                               const float (&sx)[B][NSUM], float (&acc)[B]) {
+    __device__ static void prep(const float (&x)[B][CPT], XTile<B> &t) {
+        prep_f32<FmtK45, B>(x, t);
+    }
+
+    template <int B>
+    __device__ static void dot(const Raw &w, const Lane &L, const XTile<B> &t,
+                               float (&acc)[B]) {
+        const auto &x = t.x;
+        const auto &sx = t.sx;
         const float d = f16_lo(w.h[0]), dmin = f16_hi(w.h[0]);
         uint32_t sc, mn;
         kquant_pair_scales(w.h[1], w.h[2], w.h[3], L.p, &sc, &mn);
@@ -156,7 +247,7 @@ template <int LW, bool RA> using FmtQ5K = FmtK45<LW, RA, true>;
 // qh[32h + l0 + i].  Scale of run t, element i: sc[8h + 2t + (l0+i)/16].
 // LW in {4, 8, 16, 32}.  Blocks are 210 B, so every span is realigned.
 
-template <int LW>
+template <int LW, bool IX = true>
 struct FmtQ6K {
     static_assert(LW == 4 || LW == 8 || LW == 16 || LW == 32, "tile width");
     static constexpr int QK = 256, BB = 210;
@@ -203,43 +294,22 @@ struct FmtQ6K {
         w.d = r.u16(row + L.d);
     }
 
-    template <int B>
-    __device__ static void dot(const Raw &w, const Lane &L, const float (&x)[B][CPT],
-                               const float (&)[B][NSUM], float (&acc)[B]) {
-        // Each code is assembled as the signed byte 4*(q-32): the low four
-        // bits go to bits 2..5 and the two top bits to bits 6..7 with their
-        // upper bit flipped (qh ^ 0xAA once per dword), so that the byte
-        // read as two's complement is 4*q - 128.
-        float at[4][NG][B];
-#pragma unroll
-        for (int t = 0; t < 4; t++)
-#pragma unroll
-            for (int g = 0; g < NG; g++)
-#pragma unroll
-                for (int b = 0; b < B; b++) at[t][g][b] = 0.f;
-#pragma unroll
-        for (int k = 0; k < ND; k++) {
-            const uint32_t a = w.a[k], bq = w.b[k], hx = w.h[k] ^ 0xAAAAAAAAu;
-            uint32_t q[4];
-            q[0] = opaque(((a << 2) & 0x3C3C3C3Cu) | ((hx << 6) & 0xC0C0C0C0u));
-            q[1] = opaque(((bq << 2) & 0x3C3C3C3Cu) | ((hx << 4) & 0xC0C0C0C0u));
-            q[2] = opaque(((a >> 2) & 0x3C3C3C3Cu) | ((hx << 2) & 0xC0C0C0C0u));
-            q[3] = opaque(((bq >> 2) & 0x3C3C3C3Cu) | (hx & 0xC0C0C0C0u));
-            const int g = (4 * k) / 16 < NG ? (4 * k) / 16 : 0;
-#pragma unroll
-            for (int t = 0; t < 4; t++) {
-                const float f[4] = {sbyte<0>(q[t]), sbyte<1>(q[t]), sbyte<2>(q[t]), sbyte<3>(q[t])};
-#pragma unroll
-                for (int j = 0; j < 4; j++)
-#pragma unroll
-                    for (int b = 0; b < B; b++)
-                        at[t][g][b] = fmaf(f[j], x[b][t * LW + 4 * k + j], at[t][g][b]);
-            }
-        }
-        // scale of run t, group g: byte 2t + g + l0/16 of sc[8h..8h+7]
-        const float d = f16_lo(w.d) * 0.25f;
+    // Codes of runs 0..3 for quant dword k, each as the signed byte 4*(q-32):
+    // the low four bits go to bits 2..5 and the two top bits to bits 6..7
+    // with their upper bit flipped (qh ^ 0xAA once per dword), so that the
+    // byte read as two's complement is 4*q - 128.
+    __device__ static void codes(const Raw &w, int k, uint32_t (&q)[4]) {
+        const uint32_t a = w.a[k], bq = w.b[k], hx = w.h[k] ^ 0xAAAAAAAAu;
+        q[0] = opaque(((a << 2) & 0x3C3C3C3Cu) | ((hx << 6) & 0xC0C0C0C0u));
+        q[1] = opaque(((bq << 2) & 0x3C3C3C3Cu) | ((hx << 4) & 0xC0C0C0C0u));
+        q[2] = opaque(((a >> 2) & 0x3C3C3C3Cu) | ((hx << 2) & 0xC0C0C0C0u));
+        q[3] = opaque(((bq >> 2) & 0x3C3C3C3Cu) | (hx & 0xC0C0C0C0u));
+    }
+
+    // d / 4 (the codes carry a factor 4) and the sub-block scale of run r,
+    // group g: byte 2r + g + l0/16 of sc[8h..8h+7]
+    __device__ static float scales(const Raw &w, const Lane &L, float (&sc)[4][NG]) {
         const uint32_t s0 = w.sc[0] >> (8 * L.sbyte0), s1 = w.sc[1] >> (8 * L.sbyte0);
-        float sc[4][NG];
         if constexpr (NG == 1) {
             sc[0][0] = sbyte<0>(s0);
             sc[1][0] = sbyte<2>(s0);
@@ -255,14 +325,103 @@ struct FmtQ6K {
             sc[3][0] = sbyte<2>(w.sc[1]);
             sc[3][1] = sbyte<3>(w.sc[1]);
         }
+        return f16_lo(w.d) * 0.25f;
+    }
+
+    // IX: activations as digit planes and v_dot4 on the codes (the products
+    // accumulate exactly in int32 per run and scale group); otherwise f32
+    // activations and one FMA per code.  The planes cost a conversion of
+    // the tile once per kernel, which pays off when a lane visits many rows.
+    template <int B>
+    using XTile = std::conditional_t<IX, XI8<CPT, NRUN, B>, XF32<CPT, NSUM, B>>;
+
+    template <int B>
+    __device__ static void prep(const float (&x)[B][CPT], XTile<B> &t) {
+        if constexpr (IX) {
 #pragma unroll
-        for (int t = 0; t < 4; t++)
+            for (int b = 0; b < B; b++)
 #pragma unroll
-            for (int g = 0; g < NG; g++) {
-                const float s = d * sc[t][g];
+                for (int r = 0; r < NRUN; r++)
+                    digits_run<RUNLEN>(&x[b][r * RUNLEN], &t.p[b][0][r * ND], &t.p[b][1][r * ND],
+                                       &t.p[b][2][r * ND], &t.f[b][r]);
+        } else {
+            prep_f32<FmtQ6K, B>(x, t);
+        }
+    }
+
+    template <int B>
+    __device__ static void dot(const Raw &w, const Lane &L, const XTile<B> &t,
+                               float (&acc)[B]) {
+        if constexpr (IX) {
+            int s0[4][NG][B], s1[4][NG][B], s2[4][NG][B];
 #pragma unroll
-                for (int b = 0; b < B; b++) acc[b] = fmaf(s, at[t][g][b], acc[b]);
+            for (int r = 0; r < 4; r++)
+#pragma unroll
+                for (int g = 0; g < NG; g++)
+#pragma unroll
+                    for (int b = 0; b < B; b++) s0[r][g][b] = s1[r][g][b] = s2[r][g][b] = 0;
+#pragma unroll
+            for (int k = 0; k < ND; k++) {
+                uint32_t q[4];
+                codes(w, k, q);
+                const int g = (4 * k) / 16 < NG ? (4 * k) / 16 : 0;
+#pragma unroll
+                for (int r = 0; r < 4; r++)
+#pragma unroll
+                    for (int b = 0; b < B; b++) {
+                        const int qi = (int)q[r], o = r * ND + k;
+                        s0[r][g][b] = __builtin_amdgcn_sdot4(qi, (int)t.p[b][0][o], s0[r][g][b], false);
+                        s1[r][g][b] = __builtin_amdgcn_sdot4(qi, (int)t.p[b][1][o], s1[r][g][b], false);
+                        s2[r][g][b] = __builtin_amdgcn_sdot4(qi, (int)t.p[b][2][o], s2[r][g][b], false);
+                    }
             }
+            float sc[4][NG];
+            const float d = scales(w, L, sc);
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+#pragma unroll
+                for (int g = 0; g < NG; g++) {
+                    const float ds = d * sc[r][g];
+#pragma unroll
+                    for (int b = 0; b < B; b++)
+                        acc[b] = fmaf(ds * t.f[b][r],
+                                      digits_sum(s0[r][g][b], s1[r][g][b], s2[r][g][b]), acc[b]);
+                }
+        } else {
+            float at[4][NG][B];
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+#pragma unroll
+                for (int g = 0; g < NG; g++)
+#pragma unroll
+                    for (int b = 0; b < B; b++) at[r][g][b] = 0.f;
+#pragma unroll
+            for (int k = 0; k < ND; k++) {
+                uint32_t q[4];
+                codes(w, k, q);
+                const int g = (4 * k) / 16 < NG ? (4 * k) / 16 : 0;
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const float f[4] = {sbyte<0>(q[r]), sbyte<1>(q[r]), sbyte<2>(q[r]),
+                                        sbyte<3>(q[r])};
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+#pragma unroll
+                        for (int b = 0; b < B; b++)
+                            at[r][g][b] = fmaf(f[j], t.x[b][r * LW + 4 * k + j], at[r][g][b]);
+                }
+            }
+            float sc[4][NG];
+            const float d = scales(w, L, sc);
+#pragma unroll
+            for (int r = 0; r < 4; r++)
+#pragma unroll
+                for (int g = 0; g < NG; g++) {
+                    const float ds = d * sc[r][g];
+#pragma unroll
+                    for (int b = 0; b < B; b++) acc[b] = fmaf(ds, at[r][g][b], acc[b]);
+                }
+        }
     }
 };
 
@@ -306,9 +465,16 @@ struct FmtQ80 {
         w.d = r.u16(row + L.d);
     }
 
+    template <int B> using XTile = XF32<CPT, NSUM, B>;
     template <int B>
-    __device__ static void dot(const Raw &w, const Lane &, const float (&x)[B][CPT],
-                               const float (&)[B][NSUM], float (&acc)[B]) {
+    __device__ static void prep(const float (&x)[B][CPT], XTile<B> &t) {
+        prep_f32<FmtQ80, B>(x, t);
+    }
+
+    template <int B>
+    __device__ static void dot(const Raw &w, const Lane &, const XTile<B> &t,
+                               float (&acc)[B]) {
+        const auto &x = t.x;
         float a[B];
 #pragma unroll
         for (int b = 0; b < B; b++) a[b] = 0.f;
@@ -367,9 +533,16 @@ struct FmtQ40 {
         w.d = r.u16(row + L.d);
     }
 
+    template <int B> using XTile = XF32<CPT, NSUM, B>;
     template <int B>
-    __device__ static void dot(const Raw &w, const Lane &, const float (&x)[B][CPT],
-                               const float (&)[B][NSUM], float (&acc)[B]) {
+    __device__ static void prep(const float (&x)[B][CPT], XTile<B> &t) {
+        prep_f32<FmtQ40, B>(x, t);
+    }
+
+    template <int B>
+    __device__ static void dot(const Raw &w, const Lane &, const XTile<B> &t,
+                               float (&acc)[B]) {
+        const auto &x = t.x;
         // nibble ^ 8 is nibble - 8 in 4-bit two's complement; moved to the
         // top of its byte it converts as the signed byte 16 * (nibble - 8)
         float a[B];
@@ -429,9 +602,16 @@ struct FmtF32 {
         r.template dw<ND>(row + L.off, w.v);
     }
 
+    template <int B> using XTile = XF32<CPT, NSUM, B>;
     template <int B>
-    __device__ static void dot(const Raw &w, const Lane &, const float (&x)[B][CPT],
-                               const float (&)[B][NSUM], float (&acc)[B]) {
+    __device__ static void prep(const float (&x)[B][CPT], XTile<B> &t) {
+        prep_f32<FmtF32, B>(x, t);
+    }
+
+    template <int B>
+    __device__ static void dot(const Raw &w, const Lane &, const XTile<B> &t,
+                               float (&acc)[B]) {
+        const auto &x = t.x;
 #pragma unroll
         for (int i = 0; i < ND; i++) {
             const float f = __builtin_bit_cast(float, w.v[i]);
@@ -443,12 +623,11 @@ struct FmtF32 {
 
 // Activations of one tile: x[b][run * RUNLEN + j] = X[b * xstride +
 // col0(L, run) + j] read through the buffer resource rx (4-byte-aligned
-// dword loads), plus per-run sums for the formats with a min term.  Lanes
-// without a tile hold zeros.
+// dword loads).  Lanes without a tile hold zeros.
 template <class F, int B>
 __device__ __forceinline__ void load_tile_x(rsrc_t rx, uint32_t xstride,
                                             const typename F::Lane &L, bool active,
-                                            float (&x)[B][F::CPT], float (&sx)[B][F::NSUM]) {
+                                            float (&x)[B][F::CPT]) {
 #pragma unroll
     for (int b = 0; b < B; b++) {
 #pragma unroll
@@ -463,15 +642,6 @@ __device__ __forceinline__ void load_tile_x(rsrc_t rx, uint32_t xstride,
 #pragma unroll
             for (int j = 0; j < F::RUNLEN; j++)
                 x[b][r * F::RUNLEN + j] = __builtin_bit_cast(float, v[j]);
-        }
-#pragma unroll
-        for (int s = 0; s < F::NSUM; s++) {
-            float a = 0.f;
-            if constexpr (F::NEEDS_SUM) {
-#pragma unroll
-                for (int j = 0; j < F::RUNLEN; j++) a += x[b][s * F::RUNLEN + j];
-            }
-            sx[b][s] = a;
         }
     }
 }

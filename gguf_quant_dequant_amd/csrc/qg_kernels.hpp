@@ -77,8 +77,7 @@ __device__ __forceinline__ void gemv_finish(const GemvParams &p, int64_t it, int
                                             int lane, int wave, bool active,
                                             const typename F::Lane &L,
                                             const typename F::Raw (&raw)[U],
-                                            const float (&x)[B][F::CPT],
-                                            const float (&sx)[B][F::NSUM],
+                                            const typename F::template XTile<B> &xt,
                                             float (*red)[U * B]) {
     const int64_t rg = it * ((int64_t)p.G * U) + (int64_t)grp * U;
     float acc[U * B];
@@ -87,7 +86,7 @@ __device__ __forceinline__ void gemv_finish(const GemvParams &p, int64_t it, int
         float a[B];
 #pragma unroll
         for (int b = 0; b < B; b++) a[b] = 0.f;
-        if (active && rg + u < p.rows) F::template dot<B>(raw[u], L, x, sx, a);
+        if (active && rg + u < p.rows) F::template dot<B>(raw[u], L, xt, a);
 #pragma unroll
         for (int b = 0; b < B; b++) acc[u * B + b] = a[b];
     }
@@ -139,20 +138,22 @@ __global__ void __launch_bounds__(512) qgemv_kernel(GemvParams p) {
     int64_t it = blockIdx.x;
     if (it * rpi < p.rows) gemv_issue<F, B, U>(p, it, grp, active, L, ra);
 
-    float x[B][F::CPT], sx[B][F::NSUM];
+    typename F::template XTile<B> xt;
     {
         const rsrc_t rx = make_rsrc(p.X, 4u * p.cols * (uint32_t)B);
-        load_tile_x<F, B>(rx, p.cols, L, active, x, sx);
+        float x[B][F::CPT];
+        load_tile_x<F, B>(rx, p.cols, L, active, x);
+        F::template prep<B>(x, xt);
     }
 
     __shared__ float red[8][U * B];
     while (it * rpi < p.rows) {
         if ((it + step) * rpi < p.rows) gemv_issue<F, B, U>(p, it + step, grp, active, L, rb);
-        gemv_finish<F, B, U>(p, it, grp, lig, lane, wave, active, L, ra, x, sx, red);
+        gemv_finish<F, B, U>(p, it, grp, lig, lane, wave, active, L, ra, xt, red);
         it += step;
         if (it * rpi >= p.rows) break;
         if ((it + step) * rpi < p.rows) gemv_issue<F, B, U>(p, it + step, grp, active, L, ra);
-        gemv_finish<F, B, U>(p, it, grp, lig, lane, wave, active, L, rb, x, sx, red);
+        gemv_finish<F, B, U>(p, it, grp, lig, lane, wave, active, L, rb, xt, red);
         it += step;
     }
 }
@@ -281,22 +282,7 @@ __device__ __forceinline__ void xs_read(const uint32_t *stage, uint32_t f0, uint
         }
 }
 
-template <class F, int B>
-__device__ __forceinline__ void tile_sums(const float (&x)[B][F::CPT], float (&sx)[B][F::NSUM]) {
-#pragma unroll
-    for (int b = 0; b < B; b++)
-#pragma unroll
-        for (int s = 0; s < F::NSUM; s++) {
-            float a = 0.f;
-            if constexpr (F::NEEDS_SUM) {
-#pragma unroll
-                for (int j = 0; j < F::RUNLEN; j++) a += x[b][s * F::RUNLEN + j];
-            }
-            sx[b][s] = a;
-        }
-}
-
-// Stages the xtot floats of X round by round and fills x and sx.  The
+// Stages the xtot floats of X round by round and fills x.  The
 // caller has already issued the first round's loads into xr (so that they
 // can go out ahead of its other loads).  Ends with a barrier: the stage is
 // free again on return.
@@ -305,7 +291,7 @@ __device__ __forceinline__ void xs_stage(uint32_t *stage, rsrc_t rx, uint32_t xt
                                          const uint32_t (&xbase)[B], const typename F::Lane &L,
                                          bool active, int tid, uint32_t nthr,
                                          const uint32_t (&xr)[kStageChunks][4],
-                                         float (&x)[B][F::CPT], float (&sx)[B][F::NSUM]) {
+                                         float (&x)[B][F::CPT]) {
     const uint32_t xcap = 32u * nthr;
 #pragma unroll
     for (int b = 0; b < B; b++)
@@ -324,7 +310,6 @@ __device__ __forceinline__ void xs_stage(uint32_t *stage, rsrc_t rx, uint32_t xt
         __syncthreads();
         xs_read<F, B>(stage, f0, n, xbase, L, active, x);
     }
-    tile_sums<F, B>(x, sx);
     __syncthreads();
 }
 
@@ -360,14 +345,18 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(GemvParams p) {
     StageBlock cur = stage_block(p, it, rpi);
     stage_fetch(cur, tid, nthr, reg);
 
-    float x[B][F::CPT], sx[B][F::NSUM];
-    if constexpr (XL) {
-        uint32_t xbase[B];
+    typename F::template XTile<B> xt;
+    {
+        float x[B][F::CPT];
+        if constexpr (XL) {
+            uint32_t xbase[B];
 #pragma unroll
-        for (int b = 0; b < B; b++) xbase[b] = (uint32_t)b * p.cols;
-        xs_stage<F, B>(stage, rx, xtot, xbase, L, active, tid, nthr, xr, x, sx);
-    } else {
-        load_tile_x<F, B>(rx, p.cols, L, active, x, sx);
+            for (int b = 0; b < B; b++) xbase[b] = (uint32_t)b * p.cols;
+            xs_stage<F, B>(stage, rx, xtot, xbase, L, active, tid, nthr, xr, x);
+        } else {
+            load_tile_x<F, B>(rx, p.cols, L, active, x);
+        }
+        F::template prep<B>(x, xt);
     }
     __shared__ float red[8][U * B];
 
@@ -391,7 +380,7 @@ __global__ void __launch_bounds__(512) qgemv_lds_kernel(GemvParams p) {
             if (active && rg + u < p.rows) {
                 typename F::Raw raw;
                 F::load(rd, d16 + (uint32_t)(grp * U + u) * p.row_bytes, L, raw);
-                F::template dot<B>(raw, L, x, sx, a);
+                F::template dot<B>(raw, L, xt, a);
             }
 #pragma unroll
             for (int b = 0; b < B; b++) acc[u * B + b] = a[b];
@@ -454,6 +443,28 @@ __device__ __forceinline__ bool key_before(uint32_t ah, uint32_t al, int ai, uin
 // w_s = exp(l_s - l_0) / sum_{j<k} exp(l_j - l_0), which equals the softmax
 // probabilities renormalised over the chosen set.  Lanes s < k write
 // sel[s], wout[s] (any memory space).
+// Weights of the chosen set, one wave: lane s < k holds chosen expert
+// chosen_e (rank s).  w_s = exp(l_s - l_0) / sum_{j<k} exp(l_j - l_0),
+// the softmax probabilities renormalised over the chosen set.  Lanes s < k
+// write sel[s] and wout[s].
+__device__ __forceinline__ void route_weights(const double *logits, int k, int chosen_e, int *sel,
+                                              float *wout) {
+    const int lane = __lane_id();
+    const int ce = lane < k ? chosen_e : 0;
+    const double ls = logits[ce];
+    const double l0 = __shfl(ls, 0);
+    const double ex_all = exp(ls - l0);
+    const uint64_t exb = __builtin_bit_cast(uint64_t, ex_all);
+    const uint32_t keep = lane < k ? 0xFFFFFFFFu : 0u;
+    const double ex = __builtin_bit_cast(
+        double, ((uint64_t)((uint32_t)(exb >> 32) & keep) << 32) | ((uint32_t)exb & keep));
+    const double den = wave_sum_d(ex);
+    if (lane < k) {
+        sel[lane] = chosen_e;
+        wout[lane] = (float)(ex / den);
+    }
+}
+
 template <int PER>
 __device__ void route_topk_per(const double *__restrict__ logits, int E, int k, int *sel,
                                float *wout) {
@@ -509,19 +520,7 @@ __device__ void route_topk_per(const double *__restrict__ logits, int E, int k, 
         avail &= ~mine;
         chosen_e = (lane == s) ? bi : chosen_e;
     }
-    const int ce = lane < k ? chosen_e : 0;
-    const double ls = logits[ce];
-    const double l0 = __shfl(ls, 0);
-    const double ex_all = exp(ls - l0);
-    const uint64_t exb = __builtin_bit_cast(uint64_t, ex_all);
-    const uint32_t keep = lane < k ? 0xFFFFFFFFu : 0u;
-    const double ex = __builtin_bit_cast(
-        double, ((uint64_t)((uint32_t)(exb >> 32) & keep) << 32) | ((uint32_t)exb & keep));
-    const double den = wave_sum_d(ex);
-    if (lane < k) {
-        sel[lane] = chosen_e;
-        wout[lane] = (float)(ex / den);
-    }
+    route_weights(logits, k, chosen_e, sel, wout);
 }
 
 // Each lane holds ceil(E/64) keys, rounded up to a power of two, so the k
@@ -629,10 +628,12 @@ __global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
     uint32_t xr[kStageChunks][4];
     xs_fetch(rx, 0u, (H < xcap ? H : xcap) / 4u, tid, nthr, xr);
     if (wave == 0) route_topk_wave(p.logits, p.E, p.K, s_sel, s_w);
-    float x[1][F::CPT], sx[1][F::NSUM];
+    typename F::template XTile<1> xt;
     {
         const uint32_t xbase[1] = {0u};
-        xs_stage<F, 1>(xst, rx, H, xbase, L, active, tid, nthr, xr, x, sx);
+        float x[1][F::CPT];
+        xs_stage<F, 1>(xst, rx, H, xbase, L, active, tid, nthr, xr, x);
+        F::template prep<1>(x, xt);
     }
     if (blockIdx.x == 0 && tid < p.K) {
         p.ws_sel[tid] = s_sel[tid];
@@ -664,8 +665,8 @@ __global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
         for (int u = 0; u < U; u++) {
             ag[u][0] = au[u][0] = 0.f;
             if (active && t0 + u < tasks) {
-                F::template dot<1>(rawg[u], L, x, sx, ag[u]);
-                F::template dot<1>(rawu[u], L, x, sx, au[u]);
+                F::template dot<1>(rawg[u], L, xt, ag[u]);
+                F::template dot<1>(rawu[u], L, xt, au[u]);
             }
         }
         {
@@ -746,10 +747,12 @@ __global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
     xs_fetch(ra, 0u, (xtot < xcap ? xtot : xcap) / 4u, tid, nthr, xr);
     const uint32_t expert_off =
         active ? (uint32_t)p.ws_sel[slot] * (uint32_t)p.H * p.rb_down : 0u;
-    float x[1][F::CPT], sx[1][F::NSUM];
+    typename F::template XTile<1> xt;
     {
         const uint32_t xbase[1] = {(uint32_t)slot * (uint32_t)p.F};
-        xs_stage<F, 1>(xst, ra, xtot, xbase, L, active, tid, nthr, xr, x, sx);
+        float x[1][F::CPT];
+        xs_stage<F, 1>(xst, ra, xtot, xbase, L, active, tid, nthr, xr, x);
+        F::template prep<1>(x, xt);
     }
     uint32_t dd;
     const rsrc_t rd = rows_rsrc(p.down, p.down_bytes, 0, &dd);
@@ -765,7 +768,7 @@ __global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
 #pragma unroll
         for (int u = 0; u < U; u++) {
             acc[u][0] = 0.f;
-            if (active && r0 + u < p.H) F::template dot<1>(raw[u], L, x, sx, acc[u]);
+            if (active && r0 + u < p.H) F::template dot<1>(raw[u], L, xt, acc[u]);
         }
         {
             float v[U];

@@ -78,11 +78,27 @@ def test_small_moe_every_format(gate_fmt, down_fmt):
                  f"small {gate_fmt}/{down_fmt} token {t}")
 
 
-@pytest.mark.parametrize("E,k", [(1, 1), (8, 8), (64, 1), (130, 5), (1024, 32)])
+@pytest.mark.parametrize("E,k", [(1, 1), (8, 8), (64, 1), (130, 5), (256, 32), (257, 8),
+                                  (1024, 32)])
 def test_moe_expert_counts(E, k):
     m = Moe(E=E, k=k, H=256, F=256, gate_fmt=q.QG_Q4_K, down_fmt=q.QG_Q6_K, seed=20 + E)
     g = synth.rng(21)
     _compare(m, synth.activations(g, 1, 256)[0], synth.activations(g, 1, 256)[0], f"E{E} k{k}")
+
+
+@pytest.mark.parametrize("E,k", [(24, 7), (300, 9)])
+def test_moe_tied_router_logits_pick_the_lower_index(E, k):
+    # repeated and all-zero router rows give bit-identical logits: ties
+    # across the top-k cut must go to the lower expert index
+    m = Moe(E=E, k=k, H=256, F=256, gate_fmt=q.QG_Q4_K, down_fmt=q.QG_Q6_K, seed=25 + E)
+    for e in range(E):
+        if e % 3 == 1:
+            m.router[e] = m.router[e % 5]
+        elif e % 7 == 2:
+            m.router[e] = 0.0
+    m.d_router = torch.from_numpy(m.router).to(dev())
+    g = synth.rng(26)
+    _compare(m, synth.activations(g, 1, 256)[0], synth.activations(g, 1, 256)[0], f"ties E{E}")
 
 
 def test_moe_output_may_alias_residual_and_unaligned_stacks():
