@@ -48,7 +48,48 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--moe-tokens", type=int, default=256)
     ap.add_argument("--only", default="", help="comma list of workload names (profiling)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run plain device copies of 256 MiB (scale for the HBM byte "
+                         "counters under rocprofv3 --pmc)")
     return ap.parse_args()
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_k_4096x4096_b1_hbm_traffic.md")
+KERNEL_SOURCES = ["qg_api.hip", "qg_kernels.hpp", "qg_formats.hpp", "qg_device.hpp", "qg_mfma.hpp"]
+
+
+def source_digest():
+    """sha256 over the kernel sources, to tell whether counters taken on an
+    earlier build still describe this one."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gguf_quant_dequant_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the headline kernel from the committed counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads
+    for a copy of known size); None when the summary is missing or was taken
+    on other kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel sources sha256") != source_digest():
+        return None
+    try:
+        return int(fields["HBM bytes per launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 class Gemv:
@@ -255,10 +296,19 @@ def main():
         achieved = wb / (head_us * 1e-6) / 1e9
         line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                             "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                            "traffic": None,
+                            "traffic": measured_traffic(),
                             "kernel": "qgemv_lds_kernel, Q4_K, 64-column lane tiles, batch 1",
                             "bytes_per_launch": wb}
     line["workloads"] = results
+    if args.copy_calibration:
+        n = 256 << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = n
+        del src, dst
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(line), flush=True)

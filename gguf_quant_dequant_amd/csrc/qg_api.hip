@@ -38,9 +38,6 @@ using namespace qg;
 #ifndef QG_STAGE
 #define QG_STAGE 1
 #endif
-#ifndef QG_U_STAGE
-#define QG_U_STAGE 2
-#endif
 // Block formats at batch >= QG_MX_MIN_BATCH run on the matrix cores when the
 // activation image and the stage buffers fit in LDS (0 disables).  At batch
 // 1 the VALU kernels are as fast or faster on the measured shapes.
@@ -195,6 +192,30 @@ int gemv_cpt(int fmt, int B, int64_t cols) {
     }
 }
 
+// The staged kernel with US rows per row group and stage: activations
+// through LDS when they fit one round of the stage's size, or a few rounds
+// in a workgroup that stages few row blocks (each further round adds a load
+// latency to the workgroup's start, which many blocks amortise less well
+// than the per-lane loads' uncoalesced reads).
+template <class F, int B, int US>
+void launch_staged(const GemvParams &p, const Shape &s, size_t stage_bytes, hipStream_t st) {
+    const int64_t per_iter = (int64_t)s.G * US;
+    const int64_t iters = (p.rows + per_iter - 1) / per_iter;
+    const int64_t xrounds = ((int64_t)B * p.cols + 32 * s.threads - 1) / (32 * s.threads);
+    const int grid_xl =
+        resident_grid((const void *)qgemv_lds_kernel<F, B, US, true>, s.threads, stage_bytes, iters);
+    const int64_t blocks_per_wg = (iters + grid_xl - 1) / grid_xl;
+    if (xrounds <= 1 || (xrounds <= QG_XL_ROUNDS && blocks_per_wg <= 2)) {
+        hipLaunchKernelGGL((qgemv_lds_kernel<F, B, US, true>), dim3(grid_xl), dim3(s.threads),
+                           stage_bytes, st, p);
+    } else {
+        const int grid = resident_grid((const void *)qgemv_lds_kernel<F, B, US, false>, s.threads,
+                                       stage_bytes, iters);
+        hipLaunchKernelGGL((qgemv_lds_kernel<F, B, US, false>), dim3(grid), dim3(s.threads),
+                           stage_bytes, st, p);
+    }
+}
+
 template <class F, int B, int U>
 int launch_gemv(GemvParams p, hipStream_t st) {
     p.tiles = (int32_t)(p.cols / F::CPT);
@@ -206,36 +227,24 @@ int launch_gemv(GemvParams p, hipStream_t st) {
     p.lpr = s.lpr;
     p.S = s.S;
     p.G = s.G;
-    constexpr int US = QG_U_STAGE;
-    // the stage holds kStageChunks 16-byte chunks per thread; the block's
-    // rows plus up to 15 bytes of leading alignment and the realigning
-    // reads' extra dword past the last field must fit
+    // The stage holds kStageChunks 16-byte chunks per thread; a block of
+    // G * US rows plus up to 15 bytes of leading alignment and the
+    // realigning reads' extra dword past the last field must fit.  Four rows
+    // per row group when they fit and the batch is at most 4 (more bytes in
+    // flight per workgroup for long rows; at batch 8 the extra accumulators
+    // cost occupancy), else two, else the unstaged kernel.
     const size_t stage_bytes = (size_t)kStageChunks * 16 * s.threads;
-    const bool staged =
-        QG_STAGE && (size_t)s.G * US * p.row_bytes + 15 + 4 <= stage_bytes;
-    const int u_used = staged ? US : U;
-    const int64_t per_iter = (int64_t)s.G * u_used;
-    const int64_t iters = (p.rows + per_iter - 1) / per_iter;
-    const void *k_xl = (const void *)qgemv_lds_kernel<F, B, US, true>;
-    const void *k_st = (const void *)qgemv_lds_kernel<F, B, US, false>;
-    const void *k_direct = (const void *)qgemv_kernel<F, B, U>;
-    // Activations through LDS when they fit one round of the stage's size,
-    // or a few rounds in a workgroup that stages few row blocks: each further
-    // round adds a load latency to the workgroup's start, which many blocks
-    // amortise less well than the per-lane loads' uncoalesced reads.
-    const int64_t xrounds = ((int64_t)B * p.cols + 32 * s.threads - 1) / (32 * s.threads);
-    const int grid_xl = resident_grid(k_xl, s.threads, stage_bytes, iters);
-    const int64_t blocks_per_wg = (iters + grid_xl - 1) / grid_xl;
-    const bool xl = xrounds <= 1 || (xrounds <= QG_XL_ROUNDS && blocks_per_wg <= 2);
-    if (staged && xl) {
-        hipLaunchKernelGGL((qgemv_lds_kernel<F, B, US, true>), dim3(grid_xl), dim3(s.threads),
-                           stage_bytes, st, p);
-    } else if (staged) {
-        const int grid = resident_grid(k_st, s.threads, stage_bytes, iters);
-        hipLaunchKernelGGL((qgemv_lds_kernel<F, B, US, false>), dim3(grid), dim3(s.threads),
-                           stage_bytes, st, p);
+    auto fits = [&](int us) {
+        return QG_STAGE && (size_t)s.G * us * p.row_bytes + 15 + 4 <= stage_bytes;
+    };
+    if (B <= 4 && fits(4)) {
+        launch_staged<F, B, 4>(p, s, stage_bytes, st);
+    } else if (fits(2)) {
+        launch_staged<F, B, 2>(p, s, stage_bytes, st);
     } else {
-        const int grid = resident_grid(k_direct, s.threads, 0, iters);
+        const int64_t per_iter = (int64_t)s.G * U;
+        const int64_t iters = (p.rows + per_iter - 1) / per_iter;
+        const int grid = resident_grid((const void *)qgemv_kernel<F, B, U>, s.threads, 0, iters);
         hipLaunchKernelGGL((qgemv_kernel<F, B, U>), dim3(grid), dim3(s.threads), 0, st, p);
     }
     const hipError_t e = hipGetLastError();
