@@ -127,6 +127,28 @@ def test_zero_weights_give_zero():
         assert np.array_equal(Y, np.zeros_like(Y))
 
 
+@pytest.mark.parametrize("fmt", [Q8_0, Q4_0, Q6_K])
+def test_codes_at_the_zero_point_give_exact_zero_at_batch_1(fmt):
+    # nonzero scales with every code at the format's zero point (q = 0,
+    # nibble 8, q = 32): the batch-1 kernels carry the offset exactly
+    rows, cols = 13, 512
+    W = _matrix(fmt, rows, cols, 6200 + fmt)
+    bb = q.qg_block_bytes(fmt)
+    B = W.reshape(-1, bb)
+    if fmt == Q8_0:
+        B[:, 2:34] = 0
+    elif fmt == Q4_0:
+        B[:, 2:18] = 0x88
+    else:
+        B[:, 0:128] = 0
+        B[:, 128:192] = 0xAA
+    X = synth.activations(synth.rng(6201), 1, cols)
+    Y = run_gemv(fmt, W, rows, cols, X)
+    assert np.array_equal(Y, np.zeros_like(Y))
+    Yr, A = oracle.gemv(fmt, W, rows, cols, X)
+    assert np.array_equal(Yr, np.zeros_like(Yr))
+
+
 def test_q8_0_code_minus_128():
     W = synth.matrix(synth.rng(6100), Q8_0, 4, 64)
     W[:, 2] = 0x80
