@@ -13,8 +13,10 @@ over, so each launch streams its weights from HBM.  Inputs are resident in
 HBM before the timed region starts.
 
 Timing: the K launches of a workload are captured in one HIP graph (the
-host cannot issue launches as fast as the kernels run).  The timed region
-is one replay of that graph, bracketed by torch.cuda.synchronize(): its wall
+host cannot issue launches as fast as the kernels run).  Untimed replays
+come first, for at least --warm-seconds: under sustained load the GPU takes
+a while to reach its steady clocks.  The timed region is one replay of that
+graph, bracketed by torch.cuda.synchronize(): its wall
 time gives the whole-job rate (`value`), and a HIP event pair recorded on the
 replay stream gives the average launch duration behind `roofline`.
 `cpu_baseline` times the C oracle (single thread) on a bounded sample of the
@@ -43,6 +45,9 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=2, help="untimed graph replays")
+    ap.add_argument("--warm-seconds", type=float, default=0.3,
+                    help="keep replaying untimed until this long has passed (clocks and power "
+                         "management settle under sustained load)")
     ap.add_argument("--quick", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -158,11 +163,13 @@ class Moe:
                        self.sel[t], self.w[t], self.ws, self.wsb)
 
 
-def time_launches(torch, work, steps, warmup):
+def time_launches(torch, work, steps, warmup, warm_seconds=0.0):
     """Capture `steps` back-to-back launches in one HIP graph, replay it
-    `warmup` times untimed, then time one replay: wall clock between two
-    synchronisations and a HIP event pair on the replay stream.  Returns
-    (wall seconds, event milliseconds)."""
+    `warmup` times untimed (and further until `warm_seconds` have passed:
+    the GPU reaches its sustained clocks only after some time under load),
+    then time one replay: wall clock between two synchronisations and a HIP
+    event pair on the replay stream.  Returns (wall seconds, event
+    milliseconds)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -174,9 +181,13 @@ def time_launches(torch, work, steps, warmup):
     with torch.cuda.graph(graph):
         for _ in range(steps):
             work.launch()
+    t_warm = time.perf_counter()
     for _ in range(max(1, warmup)):
         graph.replay()
     torch.cuda.synchronize()
+    while time.perf_counter() - t_warm < warm_seconds:
+        graph.replay()
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -228,7 +239,7 @@ def main():
     head = None
     if not only or "q4_k_4096x4096_b1" in only:
         head = Gemv(head_case, 1, torch, q)
-        wall, ev_ms = time_launches(torch, head, args.steps, args.warmup)
+        wall, ev_ms = time_launches(torch, head, args.steps, args.warmup, args.warm_seconds)
         per_us = ev_ms * 1e3 / args.steps
         results["q4_k_4096x4096_b1"] = dict(
             weight_bytes=head.wbytes, launches=args.steps,
@@ -249,7 +260,7 @@ def main():
             case = synth.GEMV_CASES[name]
             w = Gemv(case, b, torch, q)
             steps = max(50, min(args.steps, int(4e9 // w.wbytes)))
-            wall, ev_ms = time_launches(torch, w, steps, args.warmup)
+            wall, ev_ms = time_launches(torch, w, steps, args.warmup, args.warm_seconds)
             per_us = ev_ms * 1e3 / steps
             results[key] = dict(
                 weight_bytes=w.wbytes, launches=steps,
@@ -262,7 +273,7 @@ def main():
         if not only or "moe_ffn_qwen3_30b_a3b" in only:
             m = Moe(synth.MOE_CASE, torch, q, args.moe_tokens)
             steps = max(64, min(args.steps, 1000))
-            wall, ev_ms = time_launches(torch, m, steps, args.warmup)
+            wall, ev_ms = time_launches(torch, m, steps, args.warmup, args.warm_seconds)
             per_us = ev_ms * 1e3 / steps
             results["moe_ffn_qwen3_30b_a3b"] = dict(
                 bytes_per_token=m.bytes_per_token, tokens=steps,
