@@ -163,6 +163,65 @@ class Moe:
                        self.sel[t], self.w[t], self.ws, self.wsb)
 
 
+class MoeNorm(Moe):
+    """The MoE FFN behind the fused residual add + RMSNorm (moe_ffn_norm):
+    per token its own attention output and hidden state, one norm weight."""
+
+    def __init__(self, case, torch, q, tokens):
+        import synth
+        super().__init__(case, torch, q, tokens)
+        attn, hid, wn = synth.moe_norm_inputs(case)
+        reps = -(-tokens // attn.shape[0])
+        self.attn = torch.from_numpy(np.tile(attn, (reps, 1))[:tokens]).cuda()
+        self.hid = torch.from_numpy(np.tile(hid, (reps, 1))[:tokens]).cuda()
+        self.wn = torch.from_numpy(wn).cuda()
+        self.eps = float(np.float32(synth.NORM_EPS))
+        self.xn = torch.empty_like(self.attn)
+        self.wsb = q.moe_ffn_norm_workspace_bytes(case.hidden, case.n_experts, case.top_k,
+                                                  case.expert_dim)
+        self.ws = torch.empty(self.wsb, dtype=torch.uint8, device="cuda")
+        # plus the norm's reads: attention output, hidden state, norm weight
+        self.bytes_per_token += 3 * 4 * case.hidden
+
+    def launch(self):
+        c = self.case
+        t = self.i % self.tokens
+        r, g, u, d = self.layers[self.i % len(self.layers)]
+        self.i += 1
+        self.q.moe_ffn_norm(self.attn[t], self.hid[t], self.y[t], self.wn, self.eps, self.xn[t],
+                            r, c.gate_fmt, g, c.up_fmt, u, c.down_fmt, d, c.hidden,
+                            c.n_experts, c.top_k, c.expert_dim, self.sel[t], self.w[t],
+                            self.ws, self.wsb)
+
+
+class MoeTokens(Moe):
+    """T decode tokens per call through moe_ffn_tokens (each routed on its
+    own); the token window rotates over the 64 distinct synthetic tokens."""
+
+    def __init__(self, case, torch, q, tokens, T):
+        super().__init__(case, torch, q, tokens)
+        self.T = T
+        self.sel = torch.empty(tokens + T, case.top_k, dtype=torch.int32, device="cuda")
+        self.w = torch.empty(tokens + T, case.top_k, device="cuda")
+        self.x = torch.cat([self.x, self.x[:T]])
+        self.res = torch.cat([self.res, self.res[:T]])
+        self.y = torch.empty_like(self.x)
+        self.wsb = q.moe_ffn_tokens_workspace_bytes(T, case.n_experts, case.top_k,
+                                                    case.expert_dim)
+        self.ws = torch.empty(self.wsb, dtype=torch.uint8, device="cuda")
+
+    def launch(self):
+        c = self.case
+        t = (self.i * self.T) % self.tokens
+        r, g, u, d = self.layers[self.i % len(self.layers)]
+        self.i += 1
+        T = self.T
+        self.q.moe_ffn_tokens(self.x[t:t + T], self.res[t:t + T], self.y[t:t + T], r,
+                              c.gate_fmt, g, c.up_fmt, u, c.down_fmt, d, T, c.hidden,
+                              c.n_experts, c.top_k, c.expert_dim, self.sel[t:t + T],
+                              self.w[t:t + T], self.ws, self.wsb)
+
+
 def time_launches(torch, work, steps, warmup, warm_seconds=0.0):
     """Capture `steps` back-to-back launches in one HIP graph, replay it
     `warmup` times untimed (and further until `warm_seconds` have passed:
@@ -281,6 +340,33 @@ def main():
                 event_us_per_token=round(per_us, 3),
                 tokens_per_s=round(1e6 / per_us, 1),
                 effective_gbs=round(m.bytes_per_token / (per_us * 1e-6) / 1e9, 1))
+            del m
+        if not only or "moe_ffn_norm_qwen3_30b_a3b" in only:
+            m = MoeNorm(synth.MOE_CASE, torch, q, args.moe_tokens)
+            steps = max(64, min(args.steps, 1000))
+            wall, ev_ms = time_launches(torch, m, steps, args.warmup, args.warm_seconds)
+            per_us = ev_ms * 1e3 / steps
+            results["moe_ffn_norm_qwen3_30b_a3b"] = dict(
+                bytes_per_token=m.bytes_per_token, tokens=steps,
+                wall_tokens_per_s=round(steps / wall, 1),
+                event_us_per_token=round(per_us, 3),
+                tokens_per_s=round(1e6 / per_us, 1),
+                effective_gbs=round(m.bytes_per_token / (per_us * 1e-6) / 1e9, 1))
+            del m
+
+        for T in (4, 8):
+            key = f"moe_ffn_tokens{T}_qwen3_30b_a3b"
+            if only and key not in only:
+                continue
+            m = MoeTokens(synth.MOE_CASE, torch, q, args.moe_tokens, T)
+            steps = max(64, min(args.steps, 500))
+            wall, ev_ms = time_launches(torch, m, steps, args.warmup, args.warm_seconds)
+            per_us = ev_ms * 1e3 / steps
+            results[key] = dict(
+                tokens_per_call=T, calls=steps,
+                wall_tokens_per_s=round(steps * T / wall, 1),
+                event_us_per_call=round(per_us, 3),
+                tokens_per_s=round(T * 1e6 / per_us, 1))
             del m
 
     line = {

@@ -37,6 +37,12 @@ SIGNATURES = {
     "moe_ffn": ([_P, _P, _P, _P, _INT, _P, _INT, _P, _INT, _P, _I64, _I64, _I64, _I64,
                  _P, _P, _P, ctypes.c_size_t, _P], _INT),
     "qg_route_topk": ([_P, _I64, _I64, _P, _P, _P], _INT),
+    "moe_ffn_tokens_workspace_bytes": ([_I64, _I64, _I64, _I64], ctypes.c_size_t),
+    "moe_ffn_tokens": ([_P, _P, _P, _P, _INT, _P, _INT, _P, _INT, _P, _I64, _I64, _I64, _I64,
+                        _I64, _P, _P, _P, ctypes.c_size_t, _P], _INT),
+    "moe_ffn_norm_workspace_bytes": ([_I64, _I64, _I64, _I64], ctypes.c_size_t),
+    "moe_ffn_norm": ([_P, _P, _P, _P, ctypes.c_float, _P, _P, _INT, _P, _INT, _P, _INT, _P,
+                      _I64, _I64, _I64, _I64, _P, _P, _P, ctypes.c_size_t, _P], _INT),
 }
 
 
@@ -141,3 +147,45 @@ def qg_route_topk(logits, n_experts: int, top_k: int, sel_experts, sel_weights,
     rc = load_library().qg_route_topk(_ptr(logits), n_experts, top_k, _ptr(sel_experts),
                                       _ptr(sel_weights), _stream(stream))
     _check(rc, "qg_route_topk")
+
+
+def moe_ffn_norm_workspace_bytes(hidden: int, n_experts: int, top_k: int,
+                                 expert_dim: int) -> int:
+    return load_library().moe_ffn_norm_workspace_bytes(hidden, n_experts, top_k, expert_dim)
+
+
+def moe_ffn_norm(attn_out, hidden_in, hidden_out, norm_weight, eps: float, normed, router,
+                 gate_fmt: int, gate, up_fmt: int, up, down_fmt: int, down, hidden: int,
+                 n_experts: int, top_k: int, expert_dim: int, sel_experts=None,
+                 sel_weights=None, workspace=None, workspace_bytes: Optional[int] = None,
+                 stream=None) -> None:
+    """The MoE FFN behind the fused residual add + RMSNorm (see include/qgemv.h)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = load_library().moe_ffn_norm(_ptr(attn_out), _ptr(hidden_in), _ptr(hidden_out),
+                                     _ptr(norm_weight), float(eps), _ptr(normed), _ptr(router),
+                                     gate_fmt, _ptr(gate), up_fmt, _ptr(up), down_fmt, _ptr(down),
+                                     hidden, n_experts, top_k, expert_dim, _ptr(sel_experts),
+                                     _ptr(sel_weights), _ptr(workspace), workspace_bytes,
+                                     _stream(stream))
+    _check(rc, "moe_ffn_norm")
+
+
+def moe_ffn_tokens_workspace_bytes(tokens: int, n_experts: int, top_k: int,
+                                   expert_dim: int) -> int:
+    return load_library().moe_ffn_tokens_workspace_bytes(tokens, n_experts, top_k, expert_dim)
+
+
+def moe_ffn_tokens(x, residual, y, router, gate_fmt: int, gate, up_fmt: int, up, down_fmt: int,
+                   down, tokens: int, hidden: int, n_experts: int, top_k: int, expert_dim: int,
+                   sel_experts=None, sel_weights=None, workspace=None,
+                   workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """T decode tokens through the stacked-expert MoE FFN (see include/qgemv.h)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = load_library().moe_ffn_tokens(_ptr(x), _ptr(residual), _ptr(y), _ptr(router), gate_fmt,
+                                       _ptr(gate), up_fmt, _ptr(up), down_fmt, _ptr(down), tokens,
+                                       hidden, n_experts, top_k, expert_dim, _ptr(sel_experts),
+                                       _ptr(sel_weights), _ptr(workspace), workspace_bytes,
+                                       _stream(stream))
+    _check(rc, "moe_ffn_tokens")

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <atomic>
+#include <cmath>
 #include <map>
 #include <mutex>
 #include <tuple>
@@ -487,13 +488,15 @@ struct WsLayout {
     size_t logits, sel, w, act, total;
 };
 
-WsLayout ws_layout(int64_t E, int64_t K, int64_t F) {
+// Sections for T tokens: f64 logits [T][E], int32 routes [T][K], f32
+// weights [T][K], f32 activations [T][K][F], each 16-byte aligned.
+WsLayout ws_layout(int64_t E, int64_t K, int64_t F, int64_t T = 1) {
     WsLayout l;
     l.logits = 0;
-    l.sel = align16(8 * (size_t)E);
-    l.w = l.sel + align16(4 * (size_t)K);
-    l.act = l.w + align16(4 * (size_t)K);
-    l.total = l.act + align16(4 * (size_t)K * (size_t)F);
+    l.sel = align16(8 * (size_t)(T * E));
+    l.w = l.sel + align16(4 * (size_t)(T * K));
+    l.act = l.w + align16(4 * (size_t)(T * K));
+    l.total = l.act + align16(4 * (size_t)(T * K) * (size_t)F);
     return l;
 }
 
@@ -544,12 +547,64 @@ int launch_down(MoeParams p, hipStream_t st) {
     const int64_t per = (int64_t)s.G * U;
     const int64_t iters = (p.H + per - 1) / per;
     const size_t lds = (size_t)kStageChunks * 16 * s.threads;
-    const int grid = resident_grid((const void *)moe_down_kernel<F, U>, s.threads, lds, iters);
-    hipLaunchKernelGGL((moe_down_kernel<F, U>), dim3(grid), dim3(s.threads), lds, st, p);
+    // one grid row per token (blockIdx.y), the resident workgroups shared
+    const int64_t cap = (int64_t)device_cus() *
+                        resident_per_cu((const void *)moe_down_kernel<F, U>, s.threads, lds);
+    int64_t gx = cap / p.T;
+    gx = gx < 1 ? 1 : (gx > iters ? iters : gx);
+    hipLaunchKernelGGL((moe_down_kernel<F, U>), dim3((unsigned)gx, (unsigned)p.T), dim3(s.threads),
+                       lds, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(QG_ELAUNCH, "moe_ffn: down launch failed: %s", hipGetErrorString(e));
     return QG_OK;
+}
+
+// Several tokens: B = 4 or 8 activation vectors per tile (tokens past T
+// are zero), tile widths of the batch-B GEMV.
+template <class F, int B>
+int launch_gateup_tokens(MoeParams p, hipStream_t st) {
+    // two rows per group at B = 4; one at B = 8 (two spill registers)
+    constexpr int U = B <= 4 ? 2 : 1;
+    Shape s;
+    p.gu_tiles = p.H / F::CPT;
+    if (p.H % F::CPT != 0 || !shape_for(p.gu_tiles, &s))
+        return fail(QG_EUNSUPPORTED, "moe_ffn_tokens: hidden %d does not fit the gate/up kernel",
+                    p.H);
+    p.gu_lpr = s.lpr;
+    p.gu_S = s.S;
+    p.gu_G = s.G;
+    // at most T * K distinct experts
+    const int64_t tasks = (int64_t)p.T * p.K * p.F, per = (int64_t)s.G * U;
+    const int64_t iters = (tasks + per - 1) / per;
+    const size_t lds = (size_t)kStageChunks * 16 * s.threads;
+    const int grid =
+        resident_grid((const void *)moe_gateup_tokens_kernel<F, B, U>, s.threads, lds, iters);
+    hipLaunchKernelGGL((moe_gateup_tokens_kernel<F, B, U>), dim3(grid), dim3(s.threads), lds, st,
+                       p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(QG_ELAUNCH, "moe_ffn_tokens: gate/up launch failed: %s",
+                    hipGetErrorString(e));
+    return QG_OK;
+}
+
+template <int B>
+int dispatch_gateup_tokens_b(int fmt, const MoeParams &p, hipStream_t st) {
+    constexpr int K45 = lw_k45(B), Q6 = lw_q6k(B), Q8 = lw_q80(B), Q4 = lw_q40(B);
+    switch (fmt) {
+    case QG_Q4_K: return launch_gateup_tokens<FmtQ4K<K45, true>, B>(p, st);
+    case QG_Q5_K: return launch_gateup_tokens<FmtQ5K<K45, true>, B>(p, st);
+    case QG_Q6_K: return launch_gateup_tokens<FmtQ6K<Q6, false>, B>(p, st);
+    case QG_Q8_0: return launch_gateup_tokens<FmtQ80<Q8>, B>(p, st);
+    case QG_Q4_0: return launch_gateup_tokens<FmtQ40<Q4>, B>(p, st);
+    default: return fail(QG_EUNSUPPORTED, "moe_ffn_tokens: gate/up format %d", fmt);
+    }
+}
+
+int dispatch_gateup_tokens(int fmt, const MoeParams &p, hipStream_t st) {
+    return p.T <= 4 ? dispatch_gateup_tokens_b<4>(fmt, p, st)
+                    : dispatch_gateup_tokens_b<8>(fmt, p, st);
 }
 
 int dispatch_gateup(int fmt, const MoeParams &p, hipStream_t st) {
@@ -577,6 +632,139 @@ int dispatch_down(int fmt, const MoeParams &p, hipStream_t st) {
 }  // namespace
 
 // ========================================================================= ABI
+
+namespace {
+
+// The fused add + RMSNorm in front of the chain (moe_ffn_norm): x and
+// residual are then attn_out and hidden_in, the router kernel normalises.
+struct NormStep {
+    const float *gamma;
+    double eps;
+    float *normed;  // may be NULL
+};
+
+int moe_ffn_impl(const char *who, const float *x, const float *residual, float *y,
+                 const float *router, int gate_fmt, const void *gate, int up_fmt, const void *up,
+                 int down_fmt, const void *down, int64_t hidden, int64_t n_experts,
+                 int64_t top_k, int64_t expert_dim, int32_t *sel_experts, float *sel_weights,
+                 void *workspace, size_t workspace_bytes, void *stream, const NormStep *norm,
+                 int64_t tokens = 1) {
+    if (tokens < 1) return fail(QG_EINVAL, "%s: tokens must be positive", who);
+    if (tokens > kMaxTokens)
+        return fail(QG_EUNSUPPORTED, "%s: tokens must be in 1..%d", who, kMaxTokens);
+    if (tokens > 1 && top_k > 0 && tokens * top_k > kMaxRoutes)
+        return fail(QG_EUNSUPPORTED, "%s: tokens * top_k must be <= %d", who, kMaxRoutes);
+    if (!x || !residual || !y || !router || !gate || !up || !down || !workspace)
+        return fail(QG_EINVAL, "%s: x, residual, y, router, gate, up, down and workspace "
+                               "must be non-NULL", who);
+    if (hidden <= 0 || n_experts <= 0 || top_k <= 0 || expert_dim <= 0)
+        return fail(QG_EINVAL, "%s: sizes must be positive", who);
+    if (top_k > n_experts) return fail(QG_EINVAL, "%s: top_k %lld > n_experts %lld", who,
+                                       (long long)top_k, (long long)n_experts);
+    if (n_experts > kMaxExperts || top_k > kMaxTopK)
+        return fail(QG_EUNSUPPORTED, "%s: n_experts <= %d and top_k <= %d", who, kMaxExperts,
+                    kMaxTopK);
+    if (hidden > 65536 || expert_dim > 65536)
+        return fail(QG_EUNSUPPORTED, "%s: hidden and expert_dim must be <= 65536", who);
+    const Geom gg = geom(gate_fmt), gu = geom(up_fmt), gd = geom(down_fmt);
+    if (gg.elems == 0 || gu.elems == 0 || gd.elems == 0 || gate_fmt == QG_F32 ||
+        up_fmt == QG_F32 || down_fmt == QG_F32)
+        return fail(QG_EUNSUPPORTED, "%s: expert stacks must use a block format", who);
+    if (gate_fmt != up_fmt)
+        return fail(QG_EUNSUPPORTED, "%s: gate (%s) and up (%s) must share a format", who,
+                    fmt_name(gate_fmt), fmt_name(up_fmt));
+    if (hidden % gg.elems != 0 || expert_dim % gd.elems != 0)
+        return fail(QG_EUNSUPPORTED, "%s: hidden must be a multiple of %d and expert_dim "
+                                     "of %d", who, gg.elems, gd.elems);
+    if (!aligned_to(gate, 2) || !aligned_to(up, 2) || !aligned_to(down, 2))
+        return fail(QG_EINVAL, "%s: weight stacks must be 2-byte aligned", who);
+    if (!aligned_to(x, 4) || !aligned_to(residual, 4) || !aligned_to(y, 4) ||
+        !aligned_to(router, 4) || (sel_experts && !aligned_to(sel_experts, 4)) ||
+        (sel_weights && !aligned_to(sel_weights, 4)))
+        return fail(QG_EINVAL, "%s: float and int32 arrays must be 4-byte aligned", who);
+    if (!aligned_to(workspace, 16)) return fail(QG_EINVAL, "%s: workspace not 16-byte aligned", who);
+    if (!norm && y == x) return fail(QG_EINVAL, "%s: y must not alias x", who);
+    if (norm) {
+        if (!norm->gamma) return fail(QG_EINVAL, "%s: norm_weight must be non-NULL", who);
+        if (!aligned_to(norm->gamma, 4) || (norm->normed && !aligned_to(norm->normed, 4)))
+            return fail(QG_EINVAL, "%s: float arrays must be 4-byte aligned", who);
+        if (!(norm->eps >= 0.0) || !std::isfinite(norm->eps))
+            return fail(QG_EINVAL, "%s: eps must be finite and >= 0", who);
+        const float *nd = norm->normed;
+        if (nd && (nd == x || nd == residual || nd == y || nd == norm->gamma || nd == router))
+            return fail(QG_EINVAL, "%s: normed must not alias another argument", who);
+    }
+    const WsLayout wl = ws_layout(n_experts, top_k, expert_dim, tokens);
+    const size_t ws_need = wl.total + (norm ? align16(4 * (size_t)hidden) : 0);
+    if (workspace_bytes < ws_need)
+        return fail(QG_EINVAL, "%s: workspace of %zu bytes, %zu needed", who, workspace_bytes,
+                    ws_need);
+    const int64_t rbg = qg_row_bytes(gate_fmt, hidden), rbd = qg_row_bytes(down_fmt, expert_dim);
+    const uint64_t gate_bytes = (uint64_t)n_experts * expert_dim * rbg;
+    const uint64_t down_bytes = (uint64_t)n_experts * hidden * rbd;
+    if (gate_bytes > 0xFFFFFFFFull || down_bytes > 0xFFFFFFFFull)
+        return fail(QG_EUNSUPPORTED, "%s: each expert stack must be under 4 GiB", who);
+    if (hidden % moe_cpt(gate_fmt) != 0 || expert_dim % moe_cpt(down_fmt) != 0)
+        return fail(QG_EUNSUPPORTED, "%s: sizes do not tile", who);
+    if (hidden / moe_cpt(gate_fmt) > 512 || top_k * (expert_dim / moe_cpt(down_fmt)) > 512)
+        return fail(QG_EUNSUPPORTED, "%s: hidden or top_k * expert_dim too large", who);
+
+    uint8_t *ws = (uint8_t *)workspace;
+    MoeParams p{};
+    p.x = x;
+    p.residual = residual;
+    p.y = y;
+    p.gate = (const uint8_t *)gate;
+    p.up = (const uint8_t *)up;
+    p.down = (const uint8_t *)down;
+    p.gate_bytes = gate_bytes;
+    p.up_bytes = gate_bytes;
+    p.down_bytes = down_bytes;
+    p.rb_gate = (uint32_t)rbg;
+    p.rb_down = (uint32_t)rbd;
+    p.H = (int32_t)hidden;
+    p.E = (int32_t)n_experts;
+    p.K = (int32_t)top_k;
+    p.F = (int32_t)expert_dim;
+    p.T = (int32_t)tokens;
+    p.logits = (const double *)(ws + wl.logits);
+    p.ws_sel = (int32_t *)(ws + wl.sel);
+    p.ws_w = (float *)(ws + wl.w);
+    p.act = (float *)(ws + wl.act);
+    p.sel_out = sel_experts;
+    p.w_out = sel_weights;
+
+    hipStream_t st = (hipStream_t)stream;
+    if (norm) {
+        // x = attn_out, residual = hidden_in: the router kernel forms
+        // h = x + residual and its norm, the experts read xn (workspace),
+        // the down kernel adds h = residual + x
+        float *xn = (float *)(ws + wl.total);
+        p.x = xn;
+        p.residual2 = x;
+        hipLaunchKernelGGL(moe_norm_router_kernel, dim3((unsigned)n_experts), dim3(64), 0, st,
+                           router, x, residual, norm->gamma, norm->eps, (int)hidden,
+                           (double *)(ws + wl.logits), xn, norm->normed);
+    } else if (tokens > 1) {
+        hipLaunchKernelGGL(moe_router_tokens_kernel, dim3((unsigned)n_experts), dim3(64), 0, st,
+                           router, x, (int)tokens, (int)hidden, (int)n_experts,
+                           (double *)(ws + wl.logits));
+    } else {
+        hipLaunchKernelGGL(moe_router_kernel, dim3((unsigned)n_experts), dim3(64), 0, st, router,
+                           x, (int)hidden, (double *)(ws + wl.logits));
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return fail(QG_ELAUNCH, "%s: router launch failed: %s", who,
+                                     hipGetErrorString(e));
+    int rc = tokens > 1 ? dispatch_gateup_tokens(gate_fmt, p, st) : dispatch_gateup(gate_fmt, p, st);
+    if (rc != QG_OK) return rc;
+    rc = dispatch_down(down_fmt, p, st);
+    if (rc != QG_OK) return rc;
+    return ok();
+}
+
+
+}  // namespace
 
 extern "C" {
 
@@ -671,85 +859,45 @@ int moe_ffn(const float *x, const float *residual, float *y, const float *router
             int64_t hidden, int64_t n_experts, int64_t top_k, int64_t expert_dim,
             int32_t *sel_experts, float *sel_weights, void *workspace, size_t workspace_bytes,
             void *stream) {
-    if (!x || !residual || !y || !router || !gate || !up || !down || !workspace)
-        return fail(QG_EINVAL, "moe_ffn: x, residual, y, router, gate, up, down and workspace "
-                               "must be non-NULL");
-    if (hidden <= 0 || n_experts <= 0 || top_k <= 0 || expert_dim <= 0)
-        return fail(QG_EINVAL, "moe_ffn: sizes must be positive");
-    if (top_k > n_experts) return fail(QG_EINVAL, "moe_ffn: top_k %lld > n_experts %lld",
-                                       (long long)top_k, (long long)n_experts);
-    if (n_experts > kMaxExperts || top_k > kMaxTopK)
-        return fail(QG_EUNSUPPORTED, "moe_ffn: n_experts <= %d and top_k <= %d", kMaxExperts,
-                    kMaxTopK);
-    if (hidden > 65536 || expert_dim > 65536)
-        return fail(QG_EUNSUPPORTED, "moe_ffn: hidden and expert_dim must be <= 65536");
-    const Geom gg = geom(gate_fmt), gu = geom(up_fmt), gd = geom(down_fmt);
-    if (gg.elems == 0 || gu.elems == 0 || gd.elems == 0 || gate_fmt == QG_F32 ||
-        up_fmt == QG_F32 || down_fmt == QG_F32)
-        return fail(QG_EUNSUPPORTED, "moe_ffn: expert stacks must use a block format");
-    if (gate_fmt != up_fmt)
-        return fail(QG_EUNSUPPORTED, "moe_ffn: gate (%s) and up (%s) must share a format",
-                    fmt_name(gate_fmt), fmt_name(up_fmt));
-    if (hidden % gg.elems != 0 || expert_dim % gd.elems != 0)
-        return fail(QG_EUNSUPPORTED, "moe_ffn: hidden must be a multiple of %d and expert_dim "
-                                     "of %d", gg.elems, gd.elems);
-    if (!aligned_to(gate, 2) || !aligned_to(up, 2) || !aligned_to(down, 2))
-        return fail(QG_EINVAL, "moe_ffn: weight stacks must be 2-byte aligned");
-    if (!aligned_to(x, 4) || !aligned_to(residual, 4) || !aligned_to(y, 4) ||
-        !aligned_to(router, 4) || (sel_experts && !aligned_to(sel_experts, 4)) ||
-        (sel_weights && !aligned_to(sel_weights, 4)))
-        return fail(QG_EINVAL, "moe_ffn: float and int32 arrays must be 4-byte aligned");
-    if (!aligned_to(workspace, 16)) return fail(QG_EINVAL, "moe_ffn: workspace not 16-byte aligned");
-    if (y == x) return fail(QG_EINVAL, "moe_ffn: y must not alias x");
-    const WsLayout wl = ws_layout(n_experts, top_k, expert_dim);
-    if (workspace_bytes < wl.total)
-        return fail(QG_EINVAL, "moe_ffn: workspace of %zu bytes, %zu needed", workspace_bytes,
-                    wl.total);
-    const int64_t rbg = qg_row_bytes(gate_fmt, hidden), rbd = qg_row_bytes(down_fmt, expert_dim);
-    const uint64_t gate_bytes = (uint64_t)n_experts * expert_dim * rbg;
-    const uint64_t down_bytes = (uint64_t)n_experts * hidden * rbd;
-    if (gate_bytes > 0xFFFFFFFFull || down_bytes > 0xFFFFFFFFull)
-        return fail(QG_EUNSUPPORTED, "moe_ffn: each expert stack must be under 4 GiB");
-    if (hidden % moe_cpt(gate_fmt) != 0 || expert_dim % moe_cpt(down_fmt) != 0)
-        return fail(QG_EUNSUPPORTED, "moe_ffn: sizes do not tile");
-    if (hidden / moe_cpt(gate_fmt) > 512 || top_k * (expert_dim / moe_cpt(down_fmt)) > 512)
-        return fail(QG_EUNSUPPORTED, "moe_ffn: hidden or top_k * expert_dim too large");
+    return moe_ffn_impl("moe_ffn", x, residual, y, router, gate_fmt, gate, up_fmt, up, down_fmt,
+                        down, hidden, n_experts, top_k, expert_dim, sel_experts, sel_weights,
+                        workspace, workspace_bytes, stream, nullptr);
+}
 
-    uint8_t *ws = (uint8_t *)workspace;
-    MoeParams p{};
-    p.x = x;
-    p.residual = residual;
-    p.y = y;
-    p.gate = (const uint8_t *)gate;
-    p.up = (const uint8_t *)up;
-    p.down = (const uint8_t *)down;
-    p.gate_bytes = gate_bytes;
-    p.up_bytes = gate_bytes;
-    p.down_bytes = down_bytes;
-    p.rb_gate = (uint32_t)rbg;
-    p.rb_down = (uint32_t)rbd;
-    p.H = (int32_t)hidden;
-    p.E = (int32_t)n_experts;
-    p.K = (int32_t)top_k;
-    p.F = (int32_t)expert_dim;
-    p.logits = (const double *)(ws + wl.logits);
-    p.ws_sel = (int32_t *)(ws + wl.sel);
-    p.ws_w = (float *)(ws + wl.w);
-    p.act = (float *)(ws + wl.act);
-    p.sel_out = sel_experts;
-    p.w_out = sel_weights;
+size_t moe_ffn_tokens_workspace_bytes(int64_t tokens, int64_t n_experts, int64_t top_k,
+                                      int64_t expert_dim) {
+    if (tokens <= 0 || n_experts <= 0 || top_k <= 0 || expert_dim <= 0 || top_k > n_experts)
+        return 0;
+    return ws_layout(n_experts, top_k, expert_dim, tokens).total;
+}
 
-    hipStream_t st = (hipStream_t)stream;
-    hipLaunchKernelGGL(moe_router_kernel, dim3((unsigned)n_experts), dim3(64), 0, st, router, x,
-                       (int)hidden, (double *)(ws + wl.logits));
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return fail(QG_ELAUNCH, "moe_ffn: router launch failed: %s",
-                                     hipGetErrorString(e));
-    int rc = dispatch_gateup(gate_fmt, p, st);
-    if (rc != QG_OK) return rc;
-    rc = dispatch_down(down_fmt, p, st);
-    if (rc != QG_OK) return rc;
-    return ok();
+int moe_ffn_tokens(const float *x, const float *residual, float *y, const float *router,
+                   int gate_fmt, const void *gate, int up_fmt, const void *up, int down_fmt,
+                   const void *down, int64_t tokens, int64_t hidden, int64_t n_experts,
+                   int64_t top_k, int64_t expert_dim, int32_t *sel_experts, float *sel_weights,
+                   void *workspace, size_t workspace_bytes, void *stream) {
+    return moe_ffn_impl("moe_ffn_tokens", x, residual, y, router, gate_fmt, gate, up_fmt, up,
+                        down_fmt, down, hidden, n_experts, top_k, expert_dim, sel_experts,
+                        sel_weights, workspace, workspace_bytes, stream, nullptr, tokens);
+}
+
+size_t moe_ffn_norm_workspace_bytes(int64_t hidden, int64_t n_experts, int64_t top_k,
+                                    int64_t expert_dim) {
+    if (hidden <= 0 || n_experts <= 0 || top_k <= 0 || expert_dim <= 0 || top_k > n_experts)
+        return 0;
+    return ws_layout(n_experts, top_k, expert_dim).total + align16(4 * (size_t)hidden);
+}
+
+int moe_ffn_norm(const float *attn_out, const float *hidden_in, float *hidden_out,
+                 const float *norm_weight, float eps, float *normed, const float *router,
+                 int gate_fmt, const void *gate, int up_fmt, const void *up, int down_fmt,
+                 const void *down, int64_t hidden, int64_t n_experts, int64_t top_k,
+                 int64_t expert_dim, int32_t *sel_experts, float *sel_weights, void *workspace,
+                 size_t workspace_bytes, void *stream) {
+    const NormStep ns{norm_weight, (double)eps, normed};
+    return moe_ffn_impl("moe_ffn_norm", attn_out, hidden_in, hidden_out, router, gate_fmt, gate,
+                        up_fmt, up, down_fmt, down, hidden, n_experts, top_k, expert_dim,
+                        sel_experts, sel_weights, workspace, workspace_bytes, stream, &ns);
 }
 
 }  // extern "C"

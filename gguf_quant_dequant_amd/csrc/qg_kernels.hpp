@@ -577,9 +577,132 @@ __global__ void __launch_bounds__(64) moe_router_kernel(const float *__restrict_
     if (lane == 0) logits[e] = acc;
 }
 
+// ------------------------------------------------------- MoE K1, with norm
+//
+// Fused residual add + RMSNorm + router (web page: docs.rs, crate
+// ferrox-cuda 0.14.0, src/gpu.rs, FUSED_ADD_RMSNORM_KERNEL_SRC; the
+// aprender-serve page's moe_layer runs the norm before its router).  One
+// wave per expert, as moe_router_kernel.  Every wave forms h = a + b (f32)
+// and reduces sum h^2 in f64 with the same fixed tree, so all waves hold
+// the same inv = 1 / sqrt(sum / H + eps) without a grid-wide step; then
+// xn = (h * inv) * gamma in f64, rounded to f32, and
+// logits[e] = sum_i R[e][i] * xn[i] in f64.  Wave 0 also stores xn (to the
+// workspace, and to xn_out when given).
+__global__ void __launch_bounds__(64) moe_norm_router_kernel(
+    const float *__restrict__ R, const float *__restrict__ a, const float *__restrict__ b,
+    const float *__restrict__ gamma, double eps, int H, double *__restrict__ logits,
+    float *__restrict__ xn_ws, float *__restrict__ xn_out) {
+    const int e = blockIdx.x, lane = threadIdx.x;
+    const uint32_t hb = 4u * (uint32_t)H;
+    const rsrc_t rr = make_rsrc(R + (int64_t)e * H, hb);
+    const rsrc_t ra = make_rsrc(a, hb), rb = make_rsrc(b, hb), rg = make_rsrc(gamma, hb);
+    double acc = 0.0;
+    if (H <= 2048) {
+        // one round: every load of the wave (router row, both inputs, the
+        // norm weight) goes out before the first use; columns past H read
+        // as zero through the resources
+        uint32_t vr[8][4], va[8][4], vb[8][4], vg[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const uint32_t c = 256u * i + 4u * lane;
+            load_dw<4>(ra, 4u * c, va[i]);
+            load_dw<4>(rb, 4u * c, vb[i]);
+            load_dw<4>(rr, 4u * c, vr[i]);
+            load_dw<4>(rg, 4u * c, vg[i]);
+        }
+        float h[8][4];
+        double ss = 0.0;
+#pragma unroll
+        for (int i = 0; i < 8; i++)
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                h[i][j] =
+                    __builtin_bit_cast(float, va[i][j]) + __builtin_bit_cast(float, vb[i][j]);
+                ss = fma((double)h[i][j], (double)h[i][j], ss);
+            }
+        ss = wave_sum_d(ss);
+        const double inv = 1.0 / sqrt(ss / (double)H + eps);
+#pragma unroll
+        for (int i = 0; i < 8; i++) {
+            const int c = 256 * i + 4 * lane;
+            float xn[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                xn[j] = (float)(((double)h[i][j] * inv) *
+                                (double)__builtin_bit_cast(float, vg[i][j]));
+                acc = fma((double)__builtin_bit_cast(float, vr[i][j]), (double)xn[j], acc);
+            }
+            if (e == 0 && c < H) {
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    xn_ws[c + j] = xn[j];
+                    if (xn_out) xn_out[c + j] = xn[j];
+                }
+            }
+        }
+    } else {
+        // sum of squares over rounds of 2048 columns, then the router dot
+        // over rounds of 1024 (the inputs are read twice, from cache)
+        double ss = 0.0;
+        for (int c0 = 0; c0 < H; c0 += 2048) {
+            uint32_t va[8][4], vb[8][4];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int c = c0 + 256 * i + 4 * lane;
+                load_dw<4>(ra, 4u * c, va[i]);
+                load_dw<4>(rb, 4u * c, vb[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float h = __builtin_bit_cast(float, va[i][j]) +
+                                    __builtin_bit_cast(float, vb[i][j]);
+                    ss = fma((double)h, (double)h, ss);
+                }
+        }
+        ss = wave_sum_d(ss);
+        const double inv = 1.0 / sqrt(ss / (double)H + eps);
+        for (int c0 = 0; c0 < H; c0 += 1024) {
+            uint32_t vr[4][4], va[4][4], vb[4][4], vg[4][4];
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int c = c0 + 256 * i + 4 * lane;
+                load_dw<4>(rr, 4u * c, vr[i]);
+                load_dw<4>(ra, 4u * c, va[i]);
+                load_dw<4>(rb, 4u * c, vb[i]);
+                load_dw<4>(rg, 4u * c, vg[i]);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int c = c0 + 256 * i + 4 * lane;
+                float xn[4];
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const float h = __builtin_bit_cast(float, va[i][j]) +
+                                    __builtin_bit_cast(float, vb[i][j]);
+                    xn[j] = (float)(((double)h * inv) *
+                                    (double)__builtin_bit_cast(float, vg[i][j]));
+                    acc = fma((double)__builtin_bit_cast(float, vr[i][j]), (double)xn[j], acc);
+                }
+                if (e == 0 && c < H) {
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        xn_ws[c + j] = xn[j];
+                        if (xn_out) xn_out[c + j] = xn[j];
+                    }
+                }
+            }
+        }
+    }
+    acc = wave_sum_d(acc);
+    if (lane == 0) logits[e] = acc;
+}
+
 struct MoeParams {
     const float *x;
     const float *residual;
+    const float *residual2;  // optional: the residual is residual + residual2 (f32)
     float *y;
     const uint8_t *gate;
     const uint8_t *up;
@@ -598,7 +721,17 @@ struct MoeParams {
     int32_t gu_tiles, gu_lpr, gu_S, gu_G;
     // down kernel geometry
     int32_t dn_tiles_per_slot, dn_tiles, dn_lpr, dn_S, dn_G;
+    // tokens (moe_ffn_tokens): x, residual, y are [T][H], the routes and
+    // activations [T][K] and [T][K][F]; the down kernel takes its token
+    // from blockIdx.y
+    int32_t T;
 };
+
+// The residual stream of row r: residual[r], or the f32 sum residual[r] +
+// residual2[r] when the residual add of the norm step is fused here.
+__device__ __forceinline__ float moe_residual(const MoeParams &p, int64_t r) {
+    return p.residual2 ? p.residual[r] + p.residual2[r] : p.residual[r];
+}
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
@@ -720,6 +853,213 @@ __global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
     }
 }
 
+// ------------------------------------------------- MoE, several tokens
+//
+// moe_ffn_tokens: T <= 8 decode tokens, each routed on its own (the
+// aprender-serve page's moe_layer per token), with the expert GEMVs grouped
+// by expert so that every selected expert's gate and up rows are read once
+// for all the tokens that chose it (the batch semantics of the
+// weight_matrix.rs page's apply_batch, applied per expert).
+
+// logits[t][e] = sum_i R[e][i] * x[t][i] in f64: one wave per expert; the
+// router row is read once for all T tokens.
+__global__ void __launch_bounds__(64) moe_router_tokens_kernel(const float *__restrict__ R,
+                                                               const float *__restrict__ x,
+                                                               int T, int H, int E,
+                                                               double *__restrict__ logits) {
+    const int e = blockIdx.x, lane = threadIdx.x;
+    const rsrc_t rr = make_rsrc(R + (int64_t)e * H, 4u * (uint32_t)H);
+    const rsrc_t rx = make_rsrc(x, 4u * (uint32_t)H * (uint32_t)T);
+    double acc[8];
+#pragma unroll
+    for (int t = 0; t < 8; t++) acc[t] = 0.0;
+    // rounds of 1024 columns: the router row's and all T tokens' loads of a
+    // round are issued before its FMAs; columns past H read as zero
+    for (int c0 = 0; c0 < H; c0 += 1024) {
+        uint32_t a[4][4], b[8][4][4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const uint32_t c = (uint32_t)c0 + 256u * i + 4u * lane;
+            load_dw<4>(rr, 4u * c, a[i]);
+#pragma unroll
+            for (int t = 0; t < 8; t++)
+                if (t < T) load_dw<4>(rx, 4u * ((uint32_t)t * (uint32_t)H + c), b[t][i]);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; t++)
+            if (t < T)
+#pragma unroll
+                for (int i = 0; i < 4; i++)
+#pragma unroll
+                    for (int j = 0; j < 4; j++)
+                        acc[t] = fma((double)__builtin_bit_cast(float, a[i][j]),
+                                     (double)__builtin_bit_cast(float, b[t][i][j]), acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < 8; t++) {
+        if (t < T) {
+            const double v = wave_sum_d(acc[t]);
+            if (lane == 0) logits[(int64_t)t * E + e] = v;
+        }
+    }
+}
+
+// The distinct experts among the T*K routes, in route order (token-major,
+// then rank), and for each the slot every token holds it in (-1: none).
+// One wave; lane i holds route i (T*K <= 64).
+constexpr int kMaxTokens = 8;
+constexpr int kMaxRoutes = 64;
+
+__device__ __forceinline__ int distinct_experts(const int *s_sel, int nroutes, int K,
+                                                int *s_uexp, int (*s_uslot)[kMaxTokens]) {
+    const int lane = __lane_id();
+    const int e = lane < nroutes ? s_sel[lane] : -1 - lane;
+    int first = lane;  // lowest route index holding the same expert
+    for (int j = nroutes - 1; j >= 0; j--) {
+        const int ej = __shfl(e, j);
+        if (ej == e && j < lane) first = j;
+    }
+    const bool lead = lane < nroutes && first == lane;
+    const unsigned long long m = __ballot(lead);
+    const int u_lead = __popcll(m & ((1ull << lane) - 1ull));
+    const int u = __shfl(u_lead, first);
+    if (lead) s_uexp[u] = e;
+    if (lane < nroutes) s_uslot[u][lane / K] = lane % K;
+    return __popcll(m);
+}
+
+// Routing of all T tokens (wave t routes token t), the distinct-expert
+// table, then row tasks (distinct expert u, row j): the gate and up rows of
+// expert s_uexp[u] are read once and dotted with the B activation vectors
+// (tokens past T are zero), and every token t that chose the expert in slot
+// s gets act[t][s][j] = w[t][s] * silu(g_t) * u_t.
+template <class F, int B, int U>
+__global__ void __launch_bounds__(512) moe_gateup_tokens_kernel(MoeParams p) {
+    __shared__ int s_sel[kMaxRoutes];
+    __shared__ float s_w[kMaxRoutes];
+    __shared__ int s_uexp[kMaxRoutes];
+    __shared__ int s_uslot[kMaxRoutes][kMaxTokens];
+    __shared__ int s_nu;
+    __shared__ float red[8][2 * U * B];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    int grp, lig;
+    if (p.gu_S == 1) {
+        grp = wave * (64 / p.gu_lpr) + lane / p.gu_lpr;
+        lig = lane & (p.gu_lpr - 1);
+    } else {
+        grp = wave / p.gu_S;
+        lig = (wave % p.gu_S) * 64 + lane;
+    }
+    const bool active = lig < p.gu_tiles;
+    const typename F::Lane L = F::init(active ? lig : 0);
+    const int T = p.T, K = p.K;
+    for (int i = tid; i < kMaxRoutes * kMaxTokens; i += blockDim.x) (&s_uslot[0][0])[i] = -1;
+    // the T activation vectors are staged through LDS while the waves route
+    // (wave w takes tokens w, w + waves, ...); the staging's barriers
+    // publish the routes
+    extern __shared__ __attribute__((aligned(16))) uint32_t xst[];
+    const uint32_t nthr = blockDim.x, xcap = 32u * nthr, H = (uint32_t)p.H;
+    const uint32_t xtot = (uint32_t)T * H;
+    const rsrc_t rx = make_rsrc(p.x, 4u * xtot);
+    uint32_t xr[kStageChunks][4];
+    xs_fetch(rx, 0u, (xtot < xcap ? xtot : xcap) / 4u, tid, nthr, xr);
+    for (int t = wave; t < T; t += (int)(blockDim.x >> 6))
+        route_topk_wave(p.logits + (int64_t)t * p.E, p.E, K, s_sel + t * K, s_w + t * K);
+    typename F::template XTile<B> xt;
+    {
+        uint32_t xbase[B];
+#pragma unroll
+        for (int b = 0; b < B; b++) xbase[b] = (uint32_t)b * H;  // b >= T: past X, stays 0
+        float x[B][F::CPT];
+        xs_stage<F, B>(xst, rx, xtot, xbase, L, active, tid, nthr, xr, x);
+        F::template prep<B>(x, xt);
+    }
+    if (wave == 0) {
+        const int nu = distinct_experts(s_sel, T * K, K, s_uexp, s_uslot);
+        if (lane == 0) s_nu = nu;
+    }
+    if (blockIdx.x == 0 && tid < T * K) {
+        p.ws_sel[tid] = s_sel[tid];
+        p.ws_w[tid] = s_w[tid];
+        if (p.sel_out) p.sel_out[tid] = s_sel[tid];
+        if (p.w_out) p.w_out[tid] = s_w[tid];
+    }
+    __syncthreads();
+
+    uint32_t dg, du;
+    const rsrc_t rg = rows_rsrc(p.gate, p.gate_bytes, 0, &dg);
+    const rsrc_t ru = rows_rsrc(p.up, p.up_bytes, 0, &du);
+    const int64_t tasks = (int64_t)s_nu * p.F;
+    const int64_t tpi = (int64_t)p.gu_G * U;
+    for (int64_t it = blockIdx.x; it * tpi < tasks; it += gridDim.x) {
+        const int64_t t0 = it * tpi + (int64_t)grp * U;
+        typename F::Raw rawg[U], rawu[U];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t t = t0 + u;
+            if (active && t < tasks) {
+                const int ue = (int)(t / p.F), j = (int)(t % p.F);
+                const uint32_t off =
+                    ((uint32_t)s_uexp[ue] * (uint32_t)p.F + (uint32_t)j) * p.rb_gate;
+                F::load(BufReader{rg}, dg + off, L, rawg[u]);
+                F::load(BufReader{ru}, du + off, L, rawu[u]);
+            }
+        }
+        float v[2 * U * B];
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            float ag[B], au[B];
+#pragma unroll
+            for (int b = 0; b < B; b++) ag[b] = au[b] = 0.f;
+            if (active && t0 + u < tasks) {
+                F::template dot<B>(rawg[u], L, xt, ag);
+                F::template dot<B>(rawu[u], L, xt, au);
+            }
+#pragma unroll
+            for (int b = 0; b < B; b++) {
+                v[(2 * u) * B + b] = ag[b];
+                v[(2 * u + 1) * B + b] = au[b];
+            }
+        }
+        group_sum_all(v, p.gu_S == 1 ? p.gu_lpr : 64);
+        if (p.gu_S != 1) {
+            // the S waves of a group add their partial sums in wave order
+            if (lane == 0) {
+#pragma unroll
+                for (int i = 0; i < 2 * U * B; i++) red[wave][i] = v[i];
+            }
+            __syncthreads();
+            if (wave % p.gu_S == 0) {
+#pragma unroll
+                for (int i = 0; i < 2 * U * B; i++) {
+                    float a = 0.f;
+                    for (int w = 0; w < p.gu_S; w++) a += red[wave + w][i];
+                    v[i] = a;
+                }
+            }
+        }
+        const bool writer = p.gu_S == 1 ? lig == 0 : (wave % p.gu_S == 0 && lane == 0);
+        if (writer) {
+#pragma unroll
+            for (int u = 0; u < U; u++) {
+                const int64_t t = t0 + u;
+                if (t < tasks) {
+                    const int ue = (int)(t / p.F), j = (int)(t % p.F);
+#pragma unroll
+                    for (int b = 0; b < B; b++) {
+                        const int s = b < T ? s_uslot[ue][b] : -1;
+                        if (s >= 0)
+                            p.act[((int64_t)b * K + s) * p.F + j] =
+                                s_w[b * K + s] * silu_f(v[(2 * u) * B + b]) *
+                                v[(2 * u + 1) * B + b];
+                    }
+                }
+            }
+        }
+        if (p.gu_S != 1) __syncthreads();
+    }
+}
+
 // ------------------------------------------------------------------ MoE K3
 
 template <class F, int U>
@@ -738,6 +1078,13 @@ __global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
     const int slot = active ? lig / p.dn_tiles_per_slot : 0;
     const int tile = active ? lig % p.dn_tiles_per_slot : 0;
     const typename F::Lane L = F::init(tile);
+    // this workgroup's token: its activations, routes, residual and output
+    const int64_t tok = blockIdx.y;
+    p.act += tok * p.K * p.F;
+    p.ws_sel += tok * p.K;
+    p.y += tok * p.H;
+    p.residual += tok * p.H;
+    if (p.residual2) p.residual2 += tok * p.H;
     // the activations of all K slots, staged through LDS (coalesced loads)
     extern __shared__ __attribute__((aligned(16))) uint32_t xst[];
     const uint32_t nthr = blockDim.x, xcap = 32u * nthr;
@@ -782,7 +1129,7 @@ __global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
             if (lig == 0) {
 #pragma unroll
                 for (int u = 0; u < U; u++)
-                    if (r0 + u < p.H) p.y[r0 + u] = p.residual[r0 + u] + acc[u][0];
+                    if (r0 + u < p.H) p.y[r0 + u] = moe_residual(p, r0 + u) + acc[u][0];
             }
         } else {
             if (lane == 0) {
@@ -794,7 +1141,7 @@ __global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
                 float s = 0.f;
                 for (int w = 0; w < p.dn_S; w++) s += red[wave + w][lane];
                 const int64_t r = r0 + lane;
-                if (r < p.H) p.y[r] = p.residual[r] + s;
+                if (r < p.H) p.y[r] = moe_residual(p, r) + s;
             }
             __syncthreads();
         }

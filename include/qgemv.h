@@ -10,6 +10,10 @@
  *            F32 router GEMV, softmax / top-k / renormalise, then for every
  *            routed expert a gate GEMV, an up GEMV, SwiGLU scaled by the
  *            route weight, and a down GEMV added into the residual.
+ *   moe_ffn_norm  the same FFN behind the fused residual add + RMSNorm
+ *            that feeds its router.
+ *   moe_ffn_tokens  the same FFN for up to 8 decode tokens at once, each
+ *            routed on its own, the expert GEMVs grouped by expert.
  *
  * Sources (web pages):
  *   docs.rs, crate ferrox-cuda 0.14.0, source src/gpu.rs -- block layouts
@@ -164,6 +168,83 @@ int moe_ffn(const float *x, const float *residual, float *y,
             int64_t n_experts, int64_t top_k, int64_t expert_dim,
             int32_t *sel_experts, float *sel_weights, void *workspace,
             size_t workspace_bytes, void *stream);
+
+/* Bytes of caller-owned device workspace moe_ffn_tokens needs for T tokens
+ * (f64 logits [T][E], the routes [T][k], the activations [T][k][F]).
+ * Returns 0 for invalid sizes. */
+size_t moe_ffn_tokens_workspace_bytes(int64_t tokens, int64_t n_experts,
+                                      int64_t top_k, int64_t expert_dim);
+
+/*
+ * moe_ffn_tokens: moe_ffn for T decode tokens at once, each routed on its
+ * own (forward_qwen3_moe_resident.rs, moe_layer, per token):
+ *
+ *   y[t] = residual[t] + sum_s down[e_{t,s}] a[t][s]   for t < T,
+ *
+ * with every quantity as moe_ffn defines it for token t.  The expert GEMVs
+ * are grouped by expert: the gate and up rows of every expert that any
+ * token selected are read once and dotted with the activations of all T
+ * tokens (weight_matrix.rs apply_batch semantics), and each token that
+ * chose the expert receives its own SwiGLU activation.  The down GEMVs run
+ * per token.
+ *
+ *   x, residual, y  float [T][H]; y may alias residual, not x.
+ *   tokens       T, 1..8, with T * top_k <= 64.
+ *   sel_experts  int32 [T][k] or NULL, sel_weights float [T][k] or NULL.
+ *   workspace    moe_ffn_tokens_workspace_bytes(T, E, k, F) bytes, 16-byte
+ *                aligned; its first T * E doubles hold the logits [T][E].
+ *   Other arguments as moe_ffn.  T = 1 runs the moe_ffn kernels.
+ *   Results per token equal moe_ffn's on that token to the moe_ffn
+ *   tolerance (the expert dot products are summed with the batch-B tile
+ *   widths, a different order); the routing is identical.
+ */
+int moe_ffn_tokens(const float *x, const float *residual, float *y,
+                   const float *router, int gate_fmt, const void *gate,
+                   int up_fmt, const void *up, int down_fmt, const void *down,
+                   int64_t tokens, int64_t hidden, int64_t n_experts,
+                   int64_t top_k, int64_t expert_dim, int32_t *sel_experts,
+                   float *sel_weights, void *workspace, size_t workspace_bytes,
+                   void *stream);
+
+/* Bytes of caller-owned device workspace moe_ffn_norm needs: the moe_ffn
+ * workspace plus the H normed activations.  Returns 0 for invalid sizes. */
+size_t moe_ffn_norm_workspace_bytes(int64_t hidden, int64_t n_experts,
+                                    int64_t top_k, int64_t expert_dim);
+
+/*
+ * moe_ffn_norm: moe_ffn behind the fused residual add + RMSNorm that feeds
+ * the router (gpu.rs page, FUSED_ADD_RMSNORM_KERNEL_SRC: out = (x + r) /
+ * sqrt(mean((x + r)^2) + eps) * weight; forward_qwen3_moe_resident.rs page,
+ * moe_layer: rmsnorm(hidden, ffn_norm) feeds the router and the experts,
+ * whose outputs are added back into hidden):
+ *
+ *   h[i]   = attn_out[i] + hidden_in[i]            f32 addition
+ *   inv    = 1 / sqrt(sum_i h[i]^2 / H + eps)      f64
+ *   xn[i]  = (h[i] * inv) * norm_weight[i]         f64, rounded once to f32
+ *   hidden_out = h + sum_s down[e_s] a[s]          the moe_ffn chain on x = xn
+ *
+ *   attn_out, hidden_in, norm_weight  float [H] (device), 4-byte aligned.
+ *   eps          the norm's epsilon (>= 0, finite).
+ *   hidden_out   float [H]; may alias attn_out or hidden_in (each element
+ *                is read and then written by the same thread).
+ *   normed       float [H] or NULL: receives xn.  Must not alias any input.
+ *   The other arguments are those of moe_ffn; the workspace must hold
+ *   moe_ffn_norm_workspace_bytes(H, E, k, F) bytes, 16-byte aligned.
+ *
+ * Three kernels are enqueued: add + norm + router (every workgroup reduces
+ * the sum of squares itself, in f64, so no extra launch or grid-wide sync
+ * is needed); routing + gate/up + SwiGLU on xn; down + the residual add
+ * h = attn_out + hidden_in.  Errors as moe_ffn, plus QG_EINVAL for a
+ * negative or non-finite eps.
+ */
+int moe_ffn_norm(const float *attn_out, const float *hidden_in,
+                 float *hidden_out, const float *norm_weight, float eps,
+                 float *normed, const float *router, int gate_fmt,
+                 const void *gate, int up_fmt, const void *up, int down_fmt,
+                 const void *down, int64_t hidden, int64_t n_experts,
+                 int64_t top_k, int64_t expert_dim, int32_t *sel_experts,
+                 float *sel_weights, void *workspace, size_t workspace_bytes,
+                 void *stream);
 
 /*
  * qg_route_topk: the routing step of moe_ffn on its own, on given logits

@@ -69,6 +69,11 @@ def _load() -> ctypes.CDLL:
     lib.qref_route.restype = ci
     lib.qref_silu.argtypes = [ctypes.c_double]
     lib.qref_silu.restype = ctypes.c_double
+    lib.qref_add_rmsnorm.restype = ci
+    lib.qref_add_rmsnorm.argtypes = [P, P, P, ctypes.c_double, i64, P, P]
+    lib.qref_moe_ffn_norm.restype = ci
+    lib.qref_moe_ffn_norm.argtypes = [P, P, P, ctypes.c_double, P, ci, P, ci, P, ci, P, i64, i64,
+                                      i64, i64, P, P, P, P, P, P, P, P]
     lib.qref_moe_ffn.argtypes = [P, P, P, ci, P, ci, P, ci, P, i64, i64, i64, i64,
                                  P, P, P, P, P, P]
     lib.qref_moe_ffn.restype = ci
@@ -185,3 +190,61 @@ def moe_ffn(x, residual, router, gate_fmt, gate, up_fmt, up, down_fmt, down,
                               _ptr(sel), _ptr(w), _ptr(act))
     _check(rc, "moe_ffn")
     return dict(y=y, bound=bound, logits=logits, sel=sel, w=w, act=act)
+
+
+def add_rmsnorm(x, residual, weight, eps: float):
+    """Fused residual add + RMSNorm: (h, xn) with h = x + residual in f32 and
+    xn = (h / sqrt(mean(h^2) + eps)) * weight computed in f64, rounded to f32."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    residual = np.ascontiguousarray(residual, dtype=np.float32)
+    weight = np.ascontiguousarray(weight, dtype=np.float32)
+    n = x.shape[0]
+    h = np.empty(n, dtype=np.float32)
+    xn = np.empty(n, dtype=np.float32)
+    _check(_load().qref_add_rmsnorm(_ptr(x), _ptr(residual), _ptr(weight), float(eps), n,
+                                    _ptr(h), _ptr(xn)), "add_rmsnorm")
+    return h, xn
+
+
+def moe_ffn_norm(attn_out, hidden_in, norm_weight, eps, router, gate_fmt, gate, up_fmt, up,
+                 down_fmt, down, hidden, n_experts, top_k, expert_dim) -> dict:
+    """The MoE FFN behind the fused add + RMSNorm, everything in f64.
+
+    Returns the moe_ffn dict plus h[H] (the new residual stream before the
+    experts) and xn[H] (the normed activations the router and experts read)."""
+    attn_out = np.ascontiguousarray(attn_out, dtype=np.float32)
+    hidden_in = np.ascontiguousarray(hidden_in, dtype=np.float32)
+    norm_weight = np.ascontiguousarray(norm_weight, dtype=np.float32)
+    router = np.ascontiguousarray(router, dtype=np.float32)
+    gate = np.ascontiguousarray(gate).view(np.uint8).reshape(-1)
+    up = np.ascontiguousarray(up).view(np.uint8).reshape(-1)
+    down = np.ascontiguousarray(down).view(np.uint8).reshape(-1)
+    y = np.empty(hidden, dtype=np.float64)
+    bound = np.empty(hidden, dtype=np.float64)
+    logits = np.empty(n_experts, dtype=np.float64)
+    sel = np.empty(top_k, dtype=np.int32)
+    w = np.empty(top_k, dtype=np.float64)
+    act = np.empty((top_k, expert_dim), dtype=np.float64)
+    h = np.empty(hidden, dtype=np.float32)
+    xn = np.empty(hidden, dtype=np.float32)
+    rc = _load().qref_moe_ffn_norm(_ptr(attn_out), _ptr(hidden_in), _ptr(norm_weight), float(eps),
+                                   _ptr(router), gate_fmt, _ptr(gate), up_fmt, _ptr(up), down_fmt,
+                                   _ptr(down), hidden, n_experts, top_k, expert_dim, _ptr(y),
+                                   _ptr(bound), _ptr(logits), _ptr(sel), _ptr(w), _ptr(act),
+                                   _ptr(h), _ptr(xn))
+    _check(rc, "moe_ffn_norm")
+    return dict(y=y, bound=bound, logits=logits, sel=sel, w=w, act=act, h=h, xn=xn)
+
+
+def moe_ffn_tokens(x, residual, router, gate_fmt, gate, up_fmt, up, down_fmt, down,
+                   hidden, n_experts, top_k, expert_dim) -> dict:
+    """T decode tokens through the MoE FFN: by definition each token on its
+    own (the aprender-serve page's moe_layer runs per token), so this is
+    moe_ffn applied to every row of x [T][H] and residual [T][H].
+
+    Returns y[T][H], bound[T][H], logits[T][E], sel[T][k], w[T][k]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    residual = np.ascontiguousarray(residual, dtype=np.float32)
+    per = [moe_ffn(x[t], residual[t], router, gate_fmt, gate, up_fmt, up, down_fmt, down,
+                   hidden, n_experts, top_k, expert_dim) for t in range(x.shape[0])]
+    return {key: np.stack([r[key] for r in per]) for key in ("y", "bound", "logits", "sel", "w")}

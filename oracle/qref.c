@@ -435,3 +435,61 @@ done:
     free(logits); free(w); free(sel); free(act); free(row); free(g); free(u);
     return rc;
 }
+
+/* Fused residual add + RMSNorm, the step that feeds the router.
+ * [gpu.rs] FUSED_ADD_RMSNORM_KERNEL_SRC: out[i] = (x[i] + residual[i]) /
+ * sqrt(mean((x + residual)^2) + eps) * weight[i]; [moe.rs] moe_layer runs
+ * rmsnorm(hidden, ffn_norm) before the router and the experts, and adds the
+ * expert outputs back into hidden.
+ *   h[i]  = x[i] + residual[i]           f32 addition (the kernel's float v)
+ *   ms    = sum_i h[i]^2 / n             double, ascending i
+ *   inv   = 1 / sqrt(ms + eps)           double
+ *   xn[i] = (h[i] * inv) * weight[i]     double, rounded once to f32
+ * READING: the page's kernel computes the norm in f32 with rsqrtf; here it
+ * is computed in double and rounded to f32 once, so that the value handed
+ * to the router is the exactly rounded one.  h_out and xn_out may be NULL. */
+int qref_add_rmsnorm(const float *x, const float *residual, const float *weight, double eps,
+                     int64_t n, float *h_out, float *xn_out) {
+    int64_t i;
+    double ss = 0.0, inv;
+    if (!x || !residual || !weight || n <= 0) return QREF_EINVAL;
+    for (i = 0; i < n; i++) {
+        float h = x[i] + residual[i];
+        ss += (double)h * (double)h;
+    }
+    inv = 1.0 / sqrt(ss / (double)n + eps);
+    for (i = 0; i < n; i++) {
+        float h = x[i] + residual[i];
+        if (h_out) h_out[i] = h;
+        if (xn_out) xn_out[i] = (float)(((double)h * inv) * (double)weight[i]);
+    }
+    return QREF_OK;
+}
+
+/* The MoE FFN behind the fused add + RMSNorm ([moe.rs] moe_layer):
+ *   h  = attn_out + hidden_in, xn = rmsnorm(h) * norm_weight   (above)
+ *   y  = h + sum_s D[e_s] act[s], the experts and the router reading xn.
+ * Outputs as qref_moe_ffn, plus h_out[H] and xn_out[H] (either may be NULL). */
+int qref_moe_ffn_norm(const float *attn_out, const float *hidden_in, const float *norm_weight,
+                      double eps, const float *router, int gate_fmt, const void *gate,
+                      int up_fmt, const void *up, int down_fmt, const void *down,
+                      int64_t hidden, int64_t n_experts, int64_t top_k, int64_t expert_dim,
+                      double *y, double *bound, double *logits_out, int32_t *sel_out,
+                      double *w_out, double *act_out, float *h_out, float *xn_out) {
+    int rc;
+    float *h, *xn;
+    if (hidden <= 0) return QREF_EINVAL;
+    h = (float *)malloc(sizeof(float) * (size_t)hidden);
+    xn = (float *)malloc(sizeof(float) * (size_t)hidden);
+    if (!h || !xn) { free(h); free(xn); return QREF_EINVAL; }
+    rc = qref_add_rmsnorm(attn_out, hidden_in, norm_weight, eps, hidden, h, xn);
+    if (!rc)
+        rc = qref_moe_ffn(xn, h, router, gate_fmt, gate, up_fmt, up, down_fmt, down, hidden,
+                          n_experts, top_k, expert_dim, y, bound, logits_out, sel_out, w_out,
+                          act_out);
+    if (!rc && h_out) memcpy(h_out, h, sizeof(float) * (size_t)hidden);
+    if (!rc && xn_out) memcpy(xn_out, xn, sizeof(float) * (size_t)hidden);
+    free(h);
+    free(xn);
+    return rc;
+}

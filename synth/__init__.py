@@ -155,3 +155,18 @@ def moe_tokens(case: MoeCase, seed_offset: int = 0):
     x = activations(g, case.tokens, case.hidden)
     residual = activations(g, case.tokens, case.hidden)
     return x, residual
+
+
+# Qwen3's RMSNorm epsilon; the norm step in front of the MoE router uses it.
+NORM_EPS = 1e-6
+
+
+def moe_norm_inputs(case: MoeCase, seed_offset: int = 0):
+    """Inputs of the fused residual add + RMSNorm in front of the MoE:
+    attn_out [T][H] and hidden_in [T][H] float32 N(0, 1), and the norm
+    weight [H] float32 1 + N(0, 0.1^2)."""
+    g = rng(case.seed + 2000 + seed_offset)
+    attn = activations(g, case.tokens, case.hidden)
+    hidden = activations(g, case.tokens, case.hidden)
+    weight = (1.0 + 0.1 * g.standard_normal(case.hidden)).astype(np.float32)
+    return attn, hidden, weight

@@ -137,3 +137,84 @@ def test_missing_library_fails_loudly(tmp_path):
             q.load_library(str(tmp_path / "nope.so"))
         finally:
             q._lib = q._lib_backup
+
+
+def _norm_args(**over):
+    a = dict(attn=P, hid=P + 64, out=P + 128, gamma=P + 192, eps=1e-6, normed=P + 256, router=P,
+             gate_fmt=12, gate=P, up_fmt=12, up=P, down_fmt=14, down=P, hidden=2048,
+             n_experts=128, top_k=8, expert_dim=768, sel=P, w=P, ws=P,
+             wsb=q.moe_ffn_norm_workspace_bytes(2048, 128, 8, 768))
+    a.update(over)
+    return a
+
+
+def _call_norm(lib, a):
+    return lib.moe_ffn_norm(a["attn"], a["hid"], a["out"], a["gamma"], a["eps"], a["normed"],
+                            a["router"], a["gate_fmt"], a["gate"], a["up_fmt"], a["up"],
+                            a["down_fmt"], a["down"], a["hidden"], a["n_experts"], a["top_k"],
+                            a["expert_dim"], a["sel"], a["w"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(gamma=0), q.QG_EINVAL, "norm_weight"),
+    (dict(attn=0), q.QG_EINVAL, "non-NULL"),
+    (dict(eps=-1e-6), q.QG_EINVAL, "eps"),
+    (dict(eps=float("nan")), q.QG_EINVAL, "eps"),
+    (dict(eps=float("inf")), q.QG_EINVAL, "eps"),
+    (dict(normed=P + 192), q.QG_EINVAL, "normed"),
+    (dict(normed=P + 64), q.QG_EINVAL, "normed"),
+    (dict(gamma=P + 2), q.QG_EINVAL, "4-byte"),
+    (dict(wsb=q.moe_ffn_workspace_bytes(128, 8, 768)), q.QG_EINVAL, "workspace"),
+    (dict(top_k=33), q.QG_EUNSUPPORTED, "top_k <="),
+])
+def test_moe_ffn_norm_refuses_before_launching(lib, over, code, msg):
+    assert _call_norm(lib, _norm_args(**over)) == code
+    assert "moe_ffn_norm" in q.qg_last_error() and msg in q.qg_last_error()
+
+
+def test_norm_workspace_size(lib):
+    # the moe_ffn workspace plus H f32 normed activations, 16-byte sections
+    assert q.moe_ffn_norm_workspace_bytes(2048, 128, 8, 768) == \
+        q.moe_ffn_workspace_bytes(128, 8, 768) + 2048 * 4
+    assert q.moe_ffn_norm_workspace_bytes(100, 6, 2, 256) == \
+        q.moe_ffn_workspace_bytes(6, 2, 256) + 400
+    assert q.moe_ffn_norm_workspace_bytes(0, 6, 2, 256) == 0
+    assert q.moe_ffn_norm_workspace_bytes(256, 4, 5, 256) == 0
+
+
+def _tok_args(**over):
+    a = dict(x=P, residual=P, y=P + 64, router=P, gate_fmt=12, gate=P, up_fmt=12, up=P,
+             down_fmt=14, down=P, tokens=4, hidden=2048, n_experts=128, top_k=8,
+             expert_dim=768, sel=P, w=P, ws=P,
+             wsb=q.moe_ffn_tokens_workspace_bytes(4, 128, 8, 768))
+    a.update(over)
+    return a
+
+
+def _call_tok(lib, a):
+    return lib.moe_ffn_tokens(a["x"], a["residual"], a["y"], a["router"], a["gate_fmt"],
+                              a["gate"], a["up_fmt"], a["up"], a["down_fmt"], a["down"],
+                              a["tokens"], a["hidden"], a["n_experts"], a["top_k"],
+                              a["expert_dim"], a["sel"], a["w"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code,msg", [
+    (dict(tokens=0), q.QG_EINVAL, "tokens must be positive"),
+    (dict(tokens=9), q.QG_EUNSUPPORTED, "1..8"),
+    (dict(tokens=8, top_k=9, wsb=1 << 30), q.QG_EUNSUPPORTED, "tokens * top_k"),
+    (dict(wsb=q.moe_ffn_workspace_bytes(128, 8, 768)), q.QG_EINVAL, "workspace"),
+    (dict(x=0), q.QG_EINVAL, "non-NULL"),
+    (dict(y=P), q.QG_EINVAL, "alias"),
+])
+def test_moe_ffn_tokens_refuses_before_launching(lib, over, code, msg):
+    assert _call_tok(lib, _tok_args(**over)) == code
+    assert "moe_ffn_tokens" in q.qg_last_error() and msg in q.qg_last_error()
+
+
+def test_tokens_workspace_size(lib):
+    # T * E f64 logits, T * k routes and weights, T * k * F activations, 16-byte sections
+    assert q.moe_ffn_tokens_workspace_bytes(1, 128, 8, 768) == q.moe_ffn_workspace_bytes(128, 8, 768)
+    assert q.moe_ffn_tokens_workspace_bytes(4, 128, 8, 768) == \
+        4 * 128 * 8 + 4 * 8 * 4 + 4 * 8 * 4 + 4 * 8 * 768 * 4
+    assert q.moe_ffn_tokens_workspace_bytes(3, 6, 2, 256) == 144 + 32 + 32 + 3 * 2 * 256 * 4
+    assert q.moe_ffn_tokens_workspace_bytes(0, 6, 2, 256) == 0
