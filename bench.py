@@ -60,7 +60,8 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_k_4096x4096_b1_hbm_traffic.md")
-KERNEL_SOURCES = ["qg_api.hip", "qg_kernels.hpp", "qg_formats.hpp", "qg_device.hpp", "qg_mfma.hpp"]
+KERNEL_SOURCES = ["qg_api.hip", "qg_kernels.hpp", "qg_formats.hpp", "qg_device.hpp", "qg_mfma.hpp",
+                  "qg_q8act.hpp"]
 
 
 def source_digest():

@@ -33,6 +33,7 @@ SIGNATURES = {
     "qg_row_bytes": ([_INT, _I64], _I64),
     "qg_last_error": ([], ctypes.c_char_p),
     "qgemv": ([_INT, _P, _I64, _I64, _P, _P, _INT, _P], _INT),
+    "qgemv_q8act": ([_INT, _P, _I64, _I64, _P, _P, _P], _INT),
     "moe_ffn_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_size_t),
     "moe_ffn": ([_P, _P, _P, _P, _INT, _P, _INT, _P, _INT, _P, _I64, _I64, _I64, _I64,
                  _P, _P, _P, ctypes.c_size_t, _P], _INT),
@@ -189,3 +190,9 @@ def moe_ffn_tokens(x, residual, y, router, gate_fmt: int, gate, up_fmt: int, up,
                                        _ptr(sel_weights), _ptr(workspace), workspace_bytes,
                                        _stream(stream))
     _check(rc, "moe_ffn_tokens")
+
+
+def qgemv_q8act(fmt: int, W, rows: int, cols: int, X, Y, stream=None) -> None:
+    """Y = deq(W) * X at batch 1 on int8-quantised activations (see include/qgemv.h)."""
+    rc = load_library().qgemv_q8act(fmt, _ptr(W), rows, cols, _ptr(X), _ptr(Y), _stream(stream))
+    _check(rc, "qgemv_q8act")

@@ -8,7 +8,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "qg_api.hip")
 DEPS = [os.path.join(HERE, "csrc", f) for f in
-        ("qg_api.hip", "qg_kernels.hpp", "qg_formats.hpp", "qg_device.hpp", "qg_mfma.hpp")] + \
+        ("qg_api.hip", "qg_kernels.hpp", "qg_formats.hpp", "qg_device.hpp", "qg_mfma.hpp", "qg_q8act.hpp")] + \
        [os.path.join(ROOT, "include", "qgemv.h")]
 LIB = os.path.join(HERE, "libqgemv.so")
 ARCH = "gfx950"

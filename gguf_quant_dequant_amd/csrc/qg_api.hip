@@ -16,6 +16,7 @@
 #include "../../include/qgemv.h"
 #include "qg_kernels.hpp"
 #include "qg_mfma.hpp"
+#include "qg_q8act.hpp"
 
 using namespace qg;
 
@@ -280,6 +281,24 @@ int dispatch_gemv_b(int fmt, bool aligned, int cpt, const GemvParams &p, hipStre
     }
 }
 
+// The int8-activation variant (batch 1): the format's tiles with q8a
+// activation tiles and integer dot products.
+int dispatch_gemv_q8(int fmt, bool aligned, const GemvParams &p, hipStream_t st) {
+    constexpr int U = QG_U_B1;
+    switch (fmt) {
+    case QG_Q4_K:
+        return aligned ? launch_gemv<q8a::Q8A<FmtQ4K<32, false>>, 1, U>(p, st)
+                       : launch_gemv<q8a::Q8A<FmtQ4K<32, true>>, 1, U>(p, st);
+    case QG_Q5_K:
+        return aligned ? launch_gemv<q8a::Q8A<FmtQ5K<32, false>>, 1, U>(p, st)
+                       : launch_gemv<q8a::Q8A<FmtQ5K<32, true>>, 1, U>(p, st);
+    case QG_Q6_K: return launch_gemv<q8a::Q8A<FmtQ6K<16, false>>, 1, U>(p, st);
+    case QG_Q8_0: return launch_gemv<q8a::Q8A<FmtQ80<32>>, 1, U>(p, st);
+    case QG_Q4_0: return launch_gemv<q8a::Q8A<FmtQ40<16>>, 1, U>(p, st);
+    default: return fail(QG_EUNSUPPORTED, "qgemv_q8act: format %d has no int8 path", fmt);
+    }
+}
+
 int dispatch_gemv(int fmt, int B, bool aligned, int64_t cols, const GemvParams &p,
                   hipStream_t st) {
     const int cpt = gemv_cpt(fmt, B, cols);
@@ -401,6 +420,9 @@ bool mx_plan(const void *W, int64_t rows, int64_t cols, int batch, int64_t rb, M
     p.nbuf = nbuf;
     p.last_nblk = (int32_t)(((cols - 1) % mx::kChunk) / 32 + 1);
     p.coff = -F::OFF * 0x1p-24f;
+    p.x_stride = (uint32_t)cols;
+    p.x_bytes = (uint32_t)(4 * cols * batch);
+    p.accumulate = 0;
     pl->lds = lds;
     pl->ra = ra;
     pl->row16 = row16;
@@ -443,15 +465,60 @@ int try_mx_f(const void *W, int64_t rows, int64_t cols, const float *X, float *Y
              int64_t rb, hipStream_t st, bool *done) {
     MxPlan pl;
     *done = false;
-    if (!mx_plan<F, B>(W, rows, cols, batch, rb, &pl)) return QG_OK;
-    pl.p.X = X;
-    pl.p.Y = Y;
-    *done = true;
-    if constexpr (F::CHUNK % 4 != 0) return launch_mx_t<F, B, true, false>(pl, st);
-    else {
-        if (!pl.ra) return launch_mx_t<F, B, false, true>(pl, st);
-        return launch_mx_t<F, B, true, false>(pl, st);
+    auto launch = [&](const MxPlan &q) {
+        if constexpr (F::CHUNK % 4 != 0) return launch_mx_t<F, B, true, false>(q, st);
+        else {
+            if (!q.ra) return launch_mx_t<F, B, false, true>(q, st);
+            return launch_mx_t<F, B, true, false>(q, st);
+        }
+    };
+    if (mx_plan<F, B>(W, rows, cols, batch, rb, &pl)) {
+        pl.p.X = X;
+        pl.p.Y = Y;
+        *done = true;
+        return launch(pl);
     }
+    // The activation image of the whole row does not fit in LDS: split the
+    // columns into the fewest slices of whole 256-column chunks whose plans
+    // fit (batch >= 3 only, where the VALU kernel is compute-bound), and run
+    // them in order, each adding its sums to Y.  Every weight byte is still
+    // read once.
+    // Each slice is a launch of its own over all row tiles, so slices pay
+    // only when the tiles fill the chip (4096 rows = 128 tiles ran slower
+    // in slices than on the VALU kernel).
+    if (batch < 3 || (rows + mx::kRows - 1) / mx::kRows < device_cus()) return QG_OK;
+    const int64_t nc = (cols + mx::kChunk - 1) / mx::kChunk;
+    constexpr int kMaxSlices = 8;
+    for (int64_t ns = 2; ns <= kMaxSlices && ns <= nc; ns++) {
+        const int64_t per = (nc + ns - 1) / ns * mx::kChunk;  // columns per slice
+        MxPlan sl[kMaxSlices];
+        int n = 0;
+        bool fit = true;
+        for (int64_t c0 = 0; c0 < cols; c0 += per, n++) {
+            const int64_t pc = cols - c0 < per ? cols - c0 : per;
+            const int64_t woff = rb * c0 / cols;  // bytes of c0 columns (whole blocks)
+            const uint8_t *Wp = (const uint8_t *)W + woff;
+            if (!mx_plan<F, B>(Wp, rows, pc, batch, rb, &sl[n])) {
+                fit = false;
+                break;
+            }
+            mx::MxParams &q = sl[n].p;
+            q.w_bytes = (uint64_t)rows * (uint64_t)rb - (uint64_t)woff;
+            q.X = X + c0;
+            q.x_stride = (uint32_t)cols;
+            q.x_bytes = (uint32_t)(4 * (cols * batch - c0));
+            q.Y = Y;
+            q.accumulate = n > 0;
+        }
+        if (!fit) continue;
+        *done = true;
+        for (int i = 0; i < n; i++) {
+            const int rc = launch(sl[i]);
+            if (rc != QG_OK) return rc;
+        }
+        return QG_OK;
+    }
+    return QG_OK;
 }
 
 template <int B>
@@ -560,12 +627,11 @@ int launch_down(MoeParams p, hipStream_t st) {
     return QG_OK;
 }
 
-// Several tokens: B = 4 or 8 activation vectors per tile (tokens past T
-// are zero), tile widths of the batch-B GEMV.
+// Several tokens: B activation vectors per tile (tokens past T are zero),
+// tile widths of the batch-B GEMV.
 template <class F, int B>
 int launch_gateup_tokens(MoeParams p, hipStream_t st) {
-    // two rows per group at B = 4; one at B = 8 (two spill registers)
-    constexpr int U = B <= 4 ? 2 : 1;
+    constexpr int U = 2;
     Shape s;
     p.gu_tiles = p.H / F::CPT;
     if (p.H % F::CPT != 0 || !shape_for(p.gu_tiles, &s))
@@ -602,9 +668,26 @@ int dispatch_gateup_tokens_b(int fmt, const MoeParams &p, hipStream_t st) {
     }
 }
 
-int dispatch_gateup_tokens(int fmt, const MoeParams &p, hipStream_t st) {
-    return p.T <= 4 ? dispatch_gateup_tokens_b<4>(fmt, p, st)
-                    : dispatch_gateup_tokens_b<8>(fmt, p, st);
+// Tokens in groups of at most four, each group one launch of the B = 4
+// kernel (its own routing, distinct experts and activations).  At B = 8 the
+// tile is narrower (two waves per row group, one row per group and
+// iteration) and the kernel ran 5x slower than two B = 4 groups, whose
+// second pass re-reads the experts the groups share.
+int dispatch_gateup_tokens(int fmt, const MoeParams &p0, hipStream_t st) {
+    for (int t0 = 0; t0 < p0.T; t0 += 4) {
+        MoeParams p = p0;
+        p.T = p0.T - t0 < 4 ? p0.T - t0 : 4;
+        p.x += (int64_t)t0 * p.H;
+        p.logits += (int64_t)t0 * p.E;
+        p.ws_sel += (int64_t)t0 * p.K;
+        p.ws_w += (int64_t)t0 * p.K;
+        p.act += (int64_t)t0 * p.K * p.F;
+        if (p.sel_out) p.sel_out += (int64_t)t0 * p.K;
+        if (p.w_out) p.w_out += (int64_t)t0 * p.K;
+        const int rc = dispatch_gateup_tokens_b<4>(fmt, p, st);
+        if (rc != QG_OK) return rc;
+    }
+    return QG_OK;
 }
 
 int dispatch_gateup(int fmt, const MoeParams &p, hipStream_t st) {
@@ -828,6 +911,40 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
         if (rc != QG_OK) return rc;
     }
     return ok();
+}
+
+int qgemv_q8act(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
+                void *stream) {
+    const Geom g = geom(fmt);
+    if (g.elems == 0 || fmt == QG_F32)
+        return fail(QG_EUNSUPPORTED, "qgemv_q8act: format %d has no int8 path", fmt);
+    if (!W || !X || !Y) return fail(QG_EINVAL, "qgemv_q8act: W, X and Y must be non-NULL");
+    if (rows <= 0 || cols <= 0)
+        return fail(QG_EINVAL, "qgemv_q8act: rows (%lld) and cols (%lld) must be positive",
+                    (long long)rows, (long long)cols);
+    if (cols % g.elems != 0)
+        return fail(QG_EUNSUPPORTED, "qgemv_q8act: %s needs cols to be a multiple of %d (got %lld)",
+                    fmt_name(fmt), g.elems, (long long)cols);
+    if (!aligned_to(W, 2)) return fail(QG_EINVAL, "qgemv_q8act: W is not 2-byte aligned");
+    if (!aligned_to(X, 4) || !aligned_to(Y, 4))
+        return fail(QG_EINVAL, "qgemv_q8act: X and Y must be 4-byte aligned");
+    if (rows >= ((int64_t)1 << 31))
+        return fail(QG_EUNSUPPORTED, "qgemv_q8act: rows must be < 2^31");
+    if (cols > 65536 || !tiles_fit(fmt, 1, cols))
+        return fail(QG_EUNSUPPORTED, "qgemv_q8act: %lld columns of %s exceed the kernel's row "
+                                     "width", (long long)cols, fmt_name(fmt));
+    const int64_t rb = qg_row_bytes(fmt, cols);
+    GemvParams p{};
+    p.W = (const uint8_t *)W;
+    p.X = X;
+    p.Y = Y;
+    p.rows = rows;
+    p.w_bytes = (uint64_t)rows * (uint64_t)rb;
+    p.row_bytes = (uint32_t)rb;
+    p.cols = (uint32_t)cols;
+    p.batch_x = 1;
+    const int rc = dispatch_gemv_q8(fmt, aligned_to(W, 4) && rb % 4 == 0, p, (hipStream_t)stream);
+    return rc == QG_OK ? ok() : rc;
 }
 
 size_t moe_ffn_workspace_bytes(int64_t n_experts, int64_t top_k, int64_t expert_dim) {

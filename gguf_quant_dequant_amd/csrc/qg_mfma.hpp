@@ -101,22 +101,26 @@ __device__ __forceinline__ float group_max(float v) {
 // ------------------------------------------------------------ activations
 
 // Builds the activation image of all nc chunks in LDS (ximg), one wave per
-// (chunk, batch row).  coff = -offset * 2^-24 of the weight format; glanes
-// = lanes per code group (4 for 16-column groups, 8 for 32).  Batch rows
-// >= batch and columns >= cols read as zero.
+// (chunk, batch row).  Batch row b starts at float b * xstride of X (X may
+// be a column slice of a wider activation matrix; xbytes bounds the reads).
+// coff = -offset * 2^-24 of the weight format; glanes = lanes per code
+// group (4 for 16-column groups, 8 for 32).  Batch rows >= batch and
+// columns >= cols read as zero.
 template <int B>
-__device__ void build_ximg(const float *__restrict__ X, uint32_t cols, int batch, int nc,
-                           float coff, int glanes, uint8_t *ximg) {
+__device__ void build_ximg(const float *__restrict__ X, uint32_t cols, uint32_t xstride,
+                           uint32_t xbytes, int batch, int nc, float coff, int glanes,
+                           uint8_t *ximg) {
     constexpr int KH = kh_of(B), REC = ximg_rec(B);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const rsrc_t rx = make_rsrc(X, 4u * cols * (uint32_t)batch);
+    const rsrc_t rx = make_rsrc(X, xbytes);
     for (int u = wave; u < nc * B; u += kWaves) {
         const int c = u / B, b = u - c * B;
         const uint32_t col = (uint32_t)c * kChunk + 4u * lane;
         // columns past the row and batch rows past `batch` read as zero (an
         // out-of-range offset reads zeros without a memory access)
-        const uint32_t xo = (b < batch && col < cols) ? 4u * ((uint32_t)b * cols + col) : 0xFFFFFFF0u;
+        const uint32_t xo =
+            (b < batch && col < cols) ? 4u * ((uint32_t)b * xstride + col) : 0xFFFFFFF0u;
         const auto w = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
         float v[4];
 #pragma unroll
@@ -495,6 +499,11 @@ struct MxParams {
     int32_t nbuf;         // stage buffers (1 or 2)
     int32_t last_nblk;    // 32-column blocks in a row's last chunk (block formats)
     float coff;           // -OFF * 2^-24
+    // column slices: W and X point at the slice's first column, rows keep
+    // their full strides; the slice's sums are added to Y when accumulate
+    uint32_t x_stride;    // floats between batch rows of X
+    uint32_t x_bytes;     // readable bytes from X
+    int32_t accumulate;
 };
 
 // ROW16: row_bytes and CHUNK are multiples of 16, so every row segment of a
@@ -558,9 +567,9 @@ __global__ void __launch_bounds__(512) qgemv_mx_kernel(MxParams p) {
     // activations; a streaming one converts the activations first.
     if (p.nbuf == 1) {
         if (ns > 0) issue(0);
-        build_ximg<B>(p.X, p.cols, p.batch, p.nc, p.coff, F::GW / 4, smem);
+        build_ximg<B>(p.X, p.cols, p.x_stride, p.x_bytes, p.batch, p.nc, p.coff, F::GW / 4, smem);
     } else {
-        build_ximg<B>(p.X, p.cols, p.batch, p.nc, p.coff, F::GW / 4, smem);
+        build_ximg<B>(p.X, p.cols, p.x_stride, p.x_bytes, p.batch, p.nc, p.coff, F::GW / 4, smem);
         if (ns > 0) issue(0);
     }
     const XLane xl = make_xlane<B>(lane);
@@ -629,7 +638,10 @@ __global__ void __launch_bounds__(512) qgemv_mx_kernel(MxParams p) {
         const int k = idx / (B * kRows), rem = idx - k * B * kRows;
         const int b = rem / kRows, r = rem - b * kRows;
         const int64_t row = tile_of((int64_t)k * p.nph) * kRows + r;
-        if (b < p.batch && row < p.rows) p.Y[(int64_t)b * p.rows + row] = outb[idx];
+        if (b < p.batch && row < p.rows) {
+            float *y = p.Y + (int64_t)b * p.rows + row;
+            *y = p.accumulate ? *y + outb[idx] : outb[idx];
+        }
     }
 }
 

@@ -14,6 +14,8 @@
  *            that feeds its router.
  *   moe_ffn_tokens  the same FFN for up to 8 decode tokens at once, each
  *            routed on its own, the expert GEMVs grouped by expert.
+ *   qgemv_q8act  qgemv at batch 1 on int8-quantised activations (integer
+ *            dot products; the pages' lossy fast variant).
  *
  * Sources (web pages):
  *   docs.rs, crate ferrox-cuda 0.14.0, source src/gpu.rs -- block layouts
@@ -121,6 +123,30 @@ const char *qg_last_error(void);
  */
 int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
           float *Y, int batch, void *stream);
+
+/*
+ * qgemv_q8act: the int8-activation variant of qgemv at batch 1 -- the
+ * pages' fast variant, named there only in words (gpu.rs page, module
+ * notes: llama.cpp's integer dp4a dot product that converts to float once
+ * per block; weight_matrix.rs page, cpu_int_dot_enabled: quantise the
+ * activation to int8 and run the integer vec_dot, faster and below the f32
+ * reference's precision).
+ *
+ *   X is quantised per group of 16 consecutive columns: d = max|x| / 127,
+ *   q = rint(x / d) in f32 (round half to even; 0 for an all-zero group; a
+ *   group holding a non-finite value gives NaN outputs).  Then
+ *   Y[r] = sum_c deq(W)[r][c] * q[c] * d[c / 16], with the code products
+ *   summed exactly in int32 (v_dot4_i32_i8) per group and one f32 multiply
+ *   per group.  The result differs from qgemv's by the quantisation of X:
+ *   at most sum_c |deq(W)[r][c]| * d[c / 16] / 2 per row.
+ *
+ *   fmt    a block format (F32 is refused).  W, rows, cols, X [cols],
+ *          Y [rows] and stream as qgemv at batch 1; rows of more than 512
+ *          lane tiles (32768 columns for the K-quants, 16384 for Q8_0 and
+ *          Q4_0) are refused.  Allocates nothing.
+ */
+int qgemv_q8act(int fmt, const void *W, int64_t rows, int64_t cols,
+                const float *X, float *Y, void *stream);
 
 /* Bytes of caller-owned device workspace moe_ffn needs for these sizes
  * (f64 router logits, the k routes, the k SwiGLU activations).  Returns 0

@@ -74,6 +74,10 @@ def _load() -> ctypes.CDLL:
     lib.qref_moe_ffn_norm.restype = ci
     lib.qref_moe_ffn_norm.argtypes = [P, P, P, ctypes.c_double, P, ci, P, ci, P, ci, P, i64, i64,
                                       i64, i64, P, P, P, P, P, P, P, P]
+    lib.qref_quantize_q8.restype = ci
+    lib.qref_quantize_q8.argtypes = [P, i64, P, P]
+    lib.qref_gemv_q8act.restype = ci
+    lib.qref_gemv_q8act.argtypes = [ci, P, i64, i64, P, ci, P, P]
     lib.qref_moe_ffn.argtypes = [P, P, P, ci, P, ci, P, ci, P, i64, i64, i64, i64,
                                  P, P, P, P, P, P]
     lib.qref_moe_ffn.restype = ci
@@ -248,3 +252,28 @@ def moe_ffn_tokens(x, residual, router, gate_fmt, gate, up_fmt, up, down_fmt, do
     per = [moe_ffn(x[t], residual[t], router, gate_fmt, gate, up_fmt, up, down_fmt, down,
                    hidden, n_experts, top_k, expert_dim) for t in range(x.shape[0])]
     return {key: np.stack([r[key] for r in per]) for key in ("y", "bound", "logits", "sel", "w")}
+
+
+def quantize_q8(x):
+    """int8 activations of the int8-activation GEMV: per 16-column group,
+    d = max|x| / 127 (f32) and q = rint(x / d) (f32).  Returns (q int8 [n],
+    d float32 [n / 16])."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    n = x.shape[0]
+    q = np.empty(n, dtype=np.int8)
+    d = np.empty(n // 16, dtype=np.float32)
+    _check(_load().qref_quantize_q8(_ptr(x), n, _ptr(q), _ptr(d)), "quantize_q8")
+    return q, d
+
+
+def gemv_q8act(fmt: int, W: np.ndarray, rows: int, cols: int, X: np.ndarray):
+    """GEMV on int8-quantised activations, in f64: (Y [batch][rows], sum of
+    |w * x_q| [batch][rows])."""
+    X = np.ascontiguousarray(X, dtype=np.float32).reshape(-1, cols)
+    W = np.ascontiguousarray(W).view(np.uint8).reshape(-1)
+    batch = X.shape[0]
+    Y = np.empty((batch, rows), dtype=np.float64)
+    A = np.empty((batch, rows), dtype=np.float64)
+    _check(_load().qref_gemv_q8act(fmt, _ptr(W), rows, cols, _ptr(X), batch, _ptr(Y), _ptr(A)),
+           "gemv_q8act")
+    return Y, A

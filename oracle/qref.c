@@ -21,6 +21,7 @@
  * Parity pins for every function are in tests/test_oracle_*.py.  Readings
  * taken where the pages are silent are marked READING below.
  */
+#include <float.h>
 #include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
@@ -491,5 +492,89 @@ int qref_moe_ffn_norm(const float *attn_out, const float *hidden_in, const float
     if (!rc && xn_out) memcpy(xn_out, xn, sizeof(float) * (size_t)hidden);
     free(h);
     free(xn);
+    return rc;
+}
+
+/* Activation quantisation of the int8-activation GEMV variant.
+ * [gpu.rs] (module notes) and [wm.rs] cpu_int_dot_enabled describe the fast
+ * variant only in words: quantise the activation to int8, take integer dot
+ * products against the weight codes, convert to float once per block.
+ * READING (the pages give no layout): groups of 16 consecutive columns of
+ * each activation row; per group, in f32,
+ *   amax = max |x|,  d = amax / 127,
+ *   q    = rint(x / d)  (round half to even), 0 for every element when
+ *          amax = 0, clamped to [-127, 127];
+ * the quantised activation is q * d.  A group holding a non-finite value
+ * gets d = NaN and q = 0.  cols must be a multiple of 16.  q[cols] int8,
+ * d[cols / 16] f32 per activation row. */
+int qref_quantize_q8(const float *x, int64_t cols, int8_t *q, float *d) {
+    int64_t g, j;
+    if (!x || !q || !d || cols <= 0 || cols % 16 != 0) return QREF_EINVAL;
+    for (g = 0; g < cols / 16; g++) {
+        const float *xg = x + 16 * g;
+        float amax = 0.0f, dg;
+        int finite = 1;
+        for (j = 0; j < 16; j++) {
+            float a = fabsf(xg[j]);
+            if (!(a <= FLT_MAX)) finite = 0;
+            else if (a > amax) amax = a;
+        }
+        if (!finite) {
+            d[g] = NAN;
+            for (j = 0; j < 16; j++) q[16 * g + j] = 0;
+            continue;
+        }
+        dg = amax / 127.0f;
+        d[g] = dg;
+        for (j = 0; j < 16; j++) {
+            float v = amax == 0.0f ? 0.0f : rintf(xg[j] / dg);
+            if (v > 127.0f) v = 127.0f;
+            if (v < -127.0f) v = -127.0f;
+            q[16 * g + j] = (int8_t)v;
+        }
+    }
+    return QREF_OK;
+}
+
+/* The GEMV on quantised activations: Y[b][r] = sum_c deq(W)[r][c] *
+ * (q[b][c] * d[b][c / 16]), in double, ascending c (each product is exact:
+ * a decoded weight times a 7-bit integer times an f32 scale), with the
+ * sum of |products| in Yabs (may be NULL).  Layouts as qref_gemv. */
+int qref_gemv_q8act(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
+                    int batch, double *Y, double *Yabs) {
+    int64_t rb = qref_row_bytes(fmt, cols), r, c;
+    double *w = NULL, *xq = NULL;
+    int8_t *q = NULL;
+    float *d = NULL;
+    int b, rc = QREF_OK;
+    if (rb < 0) return qref_block_elems(fmt) ? QREF_EINVAL : QREF_EUNSUPPORTED;
+    if (!W || !X || !Y || rows <= 0 || batch <= 0 || cols % 16 != 0) return QREF_EINVAL;
+    w = (double *)malloc(sizeof(double) * (size_t)cols);
+    xq = (double *)malloc(sizeof(double) * (size_t)(cols * batch));
+    q = (int8_t *)malloc((size_t)cols);
+    d = (float *)malloc(sizeof(float) * (size_t)(cols / 16));
+    if (!w || !xq || !q || !d) { rc = QREF_EINVAL; goto done; }
+    for (b = 0; b < batch; b++) {
+        rc = qref_quantize_q8(X + (int64_t)b * cols, cols, q, d);
+        if (rc) goto done;
+        for (c = 0; c < cols; c++) xq[(int64_t)b * cols + c] = (double)q[c] * (double)d[c / 16];
+    }
+    for (r = 0; r < rows; r++) {
+        rc = qref_dequant_row(fmt, (const uint8_t *)W + r * rb, cols, w);
+        if (rc) goto done;
+        for (b = 0; b < batch; b++) {
+            double acc = 0.0, aabs = 0.0;
+            const double *xb = xq + (int64_t)b * cols;
+            for (c = 0; c < cols; c++) {
+                double p = w[c] * xb[c];
+                acc += p;
+                aabs += fabs(p);
+            }
+            Y[(int64_t)b * rows + r] = acc;
+            if (Yabs) Yabs[(int64_t)b * rows + r] = aabs;
+        }
+    }
+done:
+    free(w); free(xq); free(q); free(d);
     return rc;
 }

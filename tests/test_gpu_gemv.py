@@ -83,6 +83,18 @@ def test_wide_rows_large_batch(fmt, cols):
     _check(fmt, 23, cols, 8, 3100 + fmt)
 
 
+@pytest.mark.parametrize("fmt,cols,batch,offset", [
+    (Q5_K, 4096, 8, 0), (Q4_0, 14336, 4, 2), (Q8_0, 12320, 8, 2), (Q6_K, 6144, 5, 0),
+    (Q4_K, 8448, 3, 2),
+])
+def test_column_slices_on_the_matrix_cores(fmt, cols, batch, offset):
+    # the activation image of a whole row does not fit in LDS at this batch
+    # and the 8200 rows give 257 row tiles: the columns run as slices of
+    # whole 256-column chunks, each adding to Y (slices start at any weight
+    # alignment; a partial last tile of rows)
+    _check(fmt, 8200, cols, batch, 3400 + fmt + batch, offset=offset)
+
+
 @pytest.mark.parametrize("fmt,cols,batch", [(Q4_0, 14368, 4), (Q8_0, 12320, 3), (Q4_K, 32768, 1)])
 def test_activations_staged_in_several_rounds(fmt, cols, batch):
     # batch * cols floats exceed one round of the LDS stage (32 floats per
