@@ -101,7 +101,7 @@ def measured_traffic():
 class Gemv:
     """A GEMV workload with enough device copies of W to stay cold."""
 
-    def __init__(self, case, batch, torch, q):
+    def __init__(self, case, batch, torch, q, q8act=False):
         import synth
         self.case, self.batch, self.q, self.torch = case, batch, q, torch
         W, X = synth.gemv_inputs(case, batch)
@@ -112,12 +112,16 @@ class Gemv:
         self.X = torch.from_numpy(X).cuda()
         self.Y = torch.empty(batch, case.rows, device="cuda")
         self.i = 0
+        self.q8act = q8act
 
     def launch(self):
         W = self.copies[self.i % len(self.copies)]
         self.i += 1
-        self.q.qgemv(self.case.fmt, W, self.case.rows, self.case.cols, self.X, self.Y,
-                     self.batch)
+        if self.q8act:
+            self.q.qgemv_q8act(self.case.fmt, W, self.case.rows, self.case.cols, self.X, self.Y)
+        else:
+            self.q.qgemv(self.case.fmt, W, self.case.rows, self.case.cols, self.X, self.Y,
+                         self.batch)
 
 
 class Moe:
@@ -310,15 +314,17 @@ def main():
         del head
 
     if not args.quick:
-        sweep = [("q8_0_256x1024", 1), ("q6_k_151936x2048", 1)]
-        sweep += [("q5_k_14336x4096", b) for b in (1, 4, 8)]
-        sweep += [("q4_0_4096x14336", b) for b in (1, 4, 8)]
-        for name, b in sweep:
-            key = f"{name}_b{b}"
+        sweep = [("q8_0_256x1024", 1, False), ("q6_k_151936x2048", 1, False)]
+        sweep += [("q5_k_14336x4096", b, False) for b in (1, 4, 8)]
+        sweep += [("q4_0_4096x14336", b, False) for b in (1, 4, 8)]
+        # the int8-activation variant (batch 1)
+        sweep += [("q4_k_4096x4096", 1, True), ("q6_k_151936x2048", 1, True)]
+        for name, b, q8 in sweep:
+            key = f"{name}_b{b}" + ("_q8act" if q8 else "")
             if only and key not in only:
                 continue
             case = synth.GEMV_CASES[name]
-            w = Gemv(case, b, torch, q)
+            w = Gemv(case, b, torch, q, q8act=q8)
             steps = max(50, min(args.steps, int(4e9 // w.wbytes)))
             wall, ev_ms = time_launches(torch, w, steps, args.warmup, args.warm_seconds)
             per_us = ev_ms * 1e3 / steps

@@ -9,11 +9,11 @@
 // cpu_int_dot_enabled (quantise the activation to int8 and run the integer
 // vec_dot; faster, and it perturbs results below the f32 reference's
 // precision).  The pages give no layout for the quantised activation; the
-// one used here: groups of 16 consecutive columns, d = max|x| / 127 and
-// q = rint(x / d) in f32 (0 for an all-zero group; a group holding a
-// non-finite value gets d = NaN).  Every lane quantises the groups of its
-// own tile once per kernel: a tile is whole 16-column groups in every
-// format at batch 1.
+// one used here: groups of 16 consecutive columns, d = max|x| / 127,
+// id = 1 / d and q = rint(x * id) in f32 (0 for an all-zero group; a group
+// holding a non-finite value gets d = NaN).  One division per group.  Every
+// lane quantises the groups of its own tile once per kernel: a tile is
+// whole 16-column groups in every format at batch 1.
 //
 // Each format wrapper keeps the format's tile, loads and field decoding and
 // replaces the activation tile and the dot product.
@@ -49,13 +49,14 @@ __device__ __forceinline__ void quantize_tile(const float (&x)[CPT], XQ8<CPT> &t
         }
         const float d = amax / 127.0f;
         const bool zero = !fin || amax == 0.f;
+        const float id = zero ? 0.f : 1.0f / d;
         int sum = 0;
 #pragma unroll
         for (int k = 0; k < 4; k++) {
             uint32_t packed = 0;
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                float v = zero ? 0.f : __builtin_rintf(x[16 * g + 4 * k + i] / d);
+                float v = zero ? 0.f : __builtin_rintf(x[16 * g + 4 * k + i] * id);
                 v = v > 127.f ? 127.f : (v < -127.f ? -127.f : v);
                 const int qi = (int)v;
                 sum += qi;

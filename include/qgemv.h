@@ -133,8 +133,8 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
  * reference's precision).
  *
  *   X is quantised per group of 16 consecutive columns: d = max|x| / 127,
- *   q = rint(x / d) in f32 (round half to even; 0 for an all-zero group; a
- *   group holding a non-finite value gives NaN outputs).  Then
+ *   id = 1 / d, q = rint(x * id), all f32 (round half to even; 0 for an
+ *   all-zero group; a group holding a non-finite value gives NaN outputs).  Then
  *   Y[r] = sum_c deq(W)[r][c] * q[c] * d[c / 16], with the code products
  *   summed exactly in int32 (v_dot4_i32_i8) per group and one f32 multiply
  *   per group.  The result differs from qgemv's by the quantisation of X:

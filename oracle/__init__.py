@@ -256,7 +256,7 @@ def moe_ffn_tokens(x, residual, router, gate_fmt, gate, up_fmt, up, down_fmt, do
 
 def quantize_q8(x):
     """int8 activations of the int8-activation GEMV: per 16-column group,
-    d = max|x| / 127 (f32) and q = rint(x / d) (f32).  Returns (q int8 [n],
+    d = max|x| / 127, id = 1 / d and q = rint(x * id), all f32.  Returns (q int8 [n],
     d float32 [n / 16])."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     n = x.shape[0]

@@ -501,8 +501,8 @@ int qref_moe_ffn_norm(const float *attn_out, const float *hidden_in, const float
  * products against the weight codes, convert to float once per block.
  * READING (the pages give no layout): groups of 16 consecutive columns of
  * each activation row; per group, in f32,
- *   amax = max |x|,  d = amax / 127,
- *   q    = rint(x / d)  (round half to even), 0 for every element when
+ *   amax = max |x|,  d = amax / 127,  id = 1 / d,
+ *   q    = rint(x * id)  (round half to even), 0 for every element when
  *          amax = 0, clamped to [-127, 127];
  * the quantised activation is q * d.  A group holding a non-finite value
  * gets d = NaN and q = 0.  cols must be a multiple of 16.  q[cols] int8,
@@ -527,7 +527,8 @@ int qref_quantize_q8(const float *x, int64_t cols, int8_t *q, float *d) {
         dg = amax / 127.0f;
         d[g] = dg;
         for (j = 0; j < 16; j++) {
-            float v = amax == 0.0f ? 0.0f : rintf(xg[j] / dg);
+            float id = amax == 0.0f ? 0.0f : 1.0f / dg;
+            float v = rintf(xg[j] * id);
             if (v > 127.0f) v = 127.0f;
             if (v < -127.0f) v = -127.0f;
             q[16 * g + j] = (int8_t)v;

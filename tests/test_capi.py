@@ -218,3 +218,17 @@ def test_tokens_workspace_size(lib):
         4 * 128 * 8 + 4 * 8 * 4 + 4 * 8 * 4 + 4 * 8 * 768 * 4
     assert q.moe_ffn_tokens_workspace_bytes(3, 6, 2, 256) == 144 + 32 + 32 + 3 * 2 * 256 * 4
     assert q.moe_ffn_tokens_workspace_bytes(0, 6, 2, 256) == 0
+
+
+@pytest.mark.parametrize("args,code,msg", [
+    ((0, P, 4, 256, P, P), q.QG_EUNSUPPORTED, "no int8 path"),
+    ((12, 0, 4, 256, P, P), q.QG_EINVAL, "non-NULL"),
+    ((12, P, 0, 256, P, P), q.QG_EINVAL, "positive"),
+    ((12, P, 4, 255, P, P), q.QG_EUNSUPPORTED, "multiple of 256"),
+    ((12, P + 1, 4, 256, P, P), q.QG_EINVAL, "2-byte"),
+    ((12, P, 4, 256, P + 2, P), q.QG_EINVAL, "4-byte"),
+    ((12, P, 4, 33024, P, P), q.QG_EUNSUPPORTED, "row width"),
+])
+def test_qgemv_q8act_refuses_before_launching(lib, args, code, msg):
+    assert lib.qgemv_q8act(*args, None) == code
+    assert "qgemv_q8act" in q.qg_last_error() and msg in q.qg_last_error()

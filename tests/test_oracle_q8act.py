@@ -4,7 +4,8 @@ closed forms and against the exact GEMV oracle (no GPU).
 The pages name the variant only in words (gpu.rs page, module notes: the
 integer dp4a dot product of llama.cpp's K-quant kernels; weight_matrix.rs
 page, cpu_int_dot_enabled: quantise the activation to int8, integer
-vec_dot).  Reading: 16-column groups, d = max|x| / 127, q = rint(x / d).
+vec_dot).  Reading: 16-column groups, d = max|x| / 127, id = 1 / d,
+q = rint(x * id), all f32.
 """
 from __future__ import annotations
 
@@ -29,7 +30,7 @@ def test_representable_groups_round_trip_exactly():
 
 
 def test_rounding_is_half_to_even():
-    # amax = 127 gives d = 1: x / d is x itself
+    # amax = 127 gives d = 1 and id = 1: x * id is x itself
     x = np.zeros(16, f32)
     x[:6] = [2.5, 3.5, -2.5, -3.5, 0.5, 127.0]
     q, d = oracle.quantize_q8(x)
