@@ -317,6 +317,8 @@ def main():
         sweep = [("q8_0_256x1024", 1, False), ("q6_k_151936x2048", 1, False)]
         sweep += [("q5_k_14336x4096", b, False) for b in (1, 4, 8)]
         sweep += [("q4_0_4096x14336", b, False) for b in (1, 4, 8)]
+        # a prefill-sized batch (groups of 8 rows on the matrix cores)
+        sweep += [("q4_k_4096x4096", 32, False)]
         # the int8-activation variant (batch 1)
         sweep += [("q4_k_4096x4096", 1, True), ("q6_k_151936x2048", 1, True)]
         for name, b, q8 in sweep:

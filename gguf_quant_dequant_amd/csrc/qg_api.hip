@@ -863,6 +863,9 @@ int64_t qg_row_bytes(int fmt, int64_t cols) {
 
 const char *qg_last_error(void) { return g_err; }
 
+// Batches above 8 run as groups of 8 (see qgemv).
+constexpr int kMaxBatch = 64;
+
 int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
           int batch, void *stream) {
     const Geom g = geom(fmt);
@@ -874,7 +877,8 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
     if (cols % g.elems != 0)
         return fail(QG_EUNSUPPORTED, "qgemv: %s needs cols to be a multiple of %d (got %lld)",
                     fmt_name(fmt), g.elems, (long long)cols);
-    if (batch < 1 || batch > 8) return fail(QG_EUNSUPPORTED, "qgemv: batch %d outside 1..8", batch);
+    if (batch < 1 || batch > kMaxBatch)
+        return fail(QG_EUNSUPPORTED, "qgemv: batch %d outside 1..%d", batch, kMaxBatch);
     if (!aligned_to(W, fmt == QG_F32 ? 4 : 2))
         return fail(QG_EINVAL, "qgemv: W is not %d-byte aligned", fmt == QG_F32 ? 4 : 2);
     if (!aligned_to(X, 4) || !aligned_to(Y, 4))
@@ -885,6 +889,17 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
         return fail(QG_EUNSUPPORTED, "qgemv: F32 rows must be a multiple of 4 floats");
     const int64_t rb = qg_row_bytes(fmt, cols);
     hipStream_t st = (hipStream_t)stream;
+    if (batch > 8) {
+        // groups of up to 8 activation rows, one after another on the
+        // stream; each group streams the weights again
+        for (int b0 = 0; b0 < batch; b0 += 8) {
+            const int nb = batch - b0 < 8 ? batch - b0 : 8;
+            const int rc = qgemv(fmt, W, rows, cols, X + (int64_t)b0 * cols,
+                                 Y + (int64_t)b0 * rows, nb, stream);
+            if (rc != QG_OK) return rc;
+        }
+        return ok();
+    }
     bool done = false;
     const int mrc = try_mx(fmt, W, rows, cols, X, Y, batch, rb, st, &done);
     if (done) return mrc == QG_OK ? ok() : mrc;

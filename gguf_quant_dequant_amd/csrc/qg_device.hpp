@@ -35,23 +35,32 @@ __device__ __forceinline__ uint32_t opaque(uint32_t v) {
     return v;
 }
 
-// n consecutive dwords from a 4-byte-aligned buffer offset.
-template <int N>
+// Cache policy of the coalesced weight streams (the staged copies, where a
+// wave instruction reads whole consecutive lines): non-temporal (the nt
+// bit).  Every weight byte is read once per launch.  Measured with cold
+// weights: Q4_K 4096 x 4096 5.78 -> 5.46 us, Q6_K 151936 x 2048 51.5 ->
+// 49.4 us.  Per-lane tile loads (BufReader) keep the default policy: there
+// neighbouring lanes read parts of the same lines, and with nt the MoE
+// chain went from 25.0 to 28.9 us per token.
+constexpr int kStream = 2;
+
+// n consecutive dwords from a 4-byte-aligned buffer offset (cache policy AUX).
+template <int N, int AUX = 0>
 __device__ __forceinline__ void load_dw(rsrc_t r, uint32_t off, uint32_t *out) {
     int i = 0;
 #pragma unroll
     for (; i + 4 <= N; i += 4) {
-        auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, 0);
+        auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off + 4 * i, 0, AUX);
         out[i] = v[0]; out[i + 1] = v[1]; out[i + 2] = v[2]; out[i + 3] = v[3];
     }
     if constexpr (N % 4 == 3) {
-        auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off + 4 * i, 0, 0);
+        auto v = __builtin_amdgcn_raw_buffer_load_b96(r, off + 4 * i, 0, AUX);
         out[i] = v[0]; out[i + 1] = v[1]; out[i + 2] = v[2];
     } else if constexpr (N % 4 == 2) {
-        auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * i, 0, 0);
+        auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off + 4 * i, 0, AUX);
         out[i] = v[0]; out[i + 1] = v[1];
     } else if constexpr (N % 4 == 1) {
-        out[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, 0);
+        out[i] = __builtin_amdgcn_raw_buffer_load_b32(r, off + 4 * i, 0, AUX);
     }
 }
 
@@ -64,15 +73,15 @@ __device__ __forceinline__ void load_dw(rsrc_t r, uint32_t off, uint32_t *out) {
 // span's end, or starts past it, where it is part of the array or starts
 // out of range (read as zero, no memory access).  Without REALIGN off must
 // be a multiple of 4.
-template <int N, bool REALIGN>
+template <int N, bool REALIGN, int AUX = 0>
 __device__ __forceinline__ void load_span(rsrc_t r, uint32_t off, uint32_t *out) {
     if constexpr (!REALIGN) {
-        load_dw<N>(r, off, out);
+        load_dw<N, AUX>(r, off, out);
     } else {
         uint32_t w[N + 1];
         const uint32_t base = off & ~3u;
-        load_dw<N>(r, base, w);
-        w[N] = __builtin_amdgcn_raw_buffer_load_b32(r, base + 4u * N, 0, 0);
+        load_dw<N, AUX>(r, base, w);
+        w[N] = __builtin_amdgcn_raw_buffer_load_b32(r, base + 4u * N, 0, AUX);
         const uint32_t sel = (off & 2u) ? 0x05040302u : 0x03020100u;
 #pragma unroll
         for (int i = 0; i < N; i++) out[i] = __builtin_amdgcn_perm(w[i + 1], w[i], sel);

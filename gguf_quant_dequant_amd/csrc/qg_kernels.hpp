@@ -203,7 +203,7 @@ __device__ __forceinline__ void stage_fetch(const StageBlock &b, int tid, uint32
         // no memory traffic
         const uint32_t c = j * nthr + (uint32_t)tid;
         const uint32_t off = c < b.nch ? 16u * c : 0xFFFFFFF0u;
-        auto v = __builtin_amdgcn_raw_buffer_load_b128(b.rs, off, 0, 0);
+        auto v = __builtin_amdgcn_raw_buffer_load_b128(b.rs, off, 0, kStream);
         reg[j][0] = v[0]; reg[j][1] = v[1]; reg[j][2] = v[2]; reg[j][3] = v[3];
     }
 }

@@ -558,7 +558,7 @@ __global__ void __launch_bounds__(512) qgemv_mx_kernel(MxParams p) {
             if (tid + 512 * j < nq) {
                 const uint32_t off =
                     ROW16 ? s_src[j] + K0 : ((s_src[j] + K0 + d0) & ~15u) + s_u[j];
-                stg[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0);
+                stg[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kStream);
             }
         }
     };

@@ -106,8 +106,11 @@ const char *qg_last_error(void);
  *   cols   > 0, a multiple of qg_block_elems(fmt).
  *   X      float [batch][cols], 4-byte aligned.
  *   Y      float [batch][rows], 4-byte aligned; must not overlap W or X.
- *   batch  1..8.  Every weight byte is read from memory once and used for
- *          all batch columns (weight_matrix.rs apply_batch).
+ *   batch  1..64.  Up to 8, every weight byte is read from memory once and
+ *          used for all batch rows (weight_matrix.rs apply_batch).  Above 8
+ *          the rows run as groups of 8, one after another on the stream,
+ *          and each group streams the weights again (prefill-sized batches;
+ *          results per row as at batch <= 8).
  *   stream hipStream_t or NULL.
  *
  * Dequantisation per element follows the block layouts of the gpu.rs page

@@ -60,7 +60,8 @@ P = 0x10000  # a fake, aligned, never-dereferenced pointer value
     ((12, P, 4, 255, P, P, 1), q.QG_EUNSUPPORTED, "multiple of 256"),
     ((2, P, 4, 48, P, P, 1), q.QG_EUNSUPPORTED, "multiple of 32"),
     ((12, P, 4, 256, P, P, 0), q.QG_EUNSUPPORTED, "batch"),
-    ((12, P, 4, 256, P, P, 9), q.QG_EUNSUPPORTED, "batch"),
+    ((12, P, 4, 256, P, P, 65), q.QG_EUNSUPPORTED, "batch"),
+    ((12, P, 4, 256, P, P, 0), q.QG_EUNSUPPORTED, "batch"),
     ((5, P, 4, 256, P, P, 1), q.QG_EUNSUPPORTED, "unknown format"),
     ((12, P + 1, 4, 256, P, P, 1), q.QG_EINVAL, "aligned"),
     ((0, P + 2, 4, 256, P, P, 1), q.QG_EINVAL, "aligned"),

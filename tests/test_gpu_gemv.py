@@ -83,6 +83,22 @@ def test_wide_rows_large_batch(fmt, cols):
     _check(fmt, 23, cols, 8, 3100 + fmt)
 
 
+@pytest.mark.parametrize("fmt", [Q8_0, Q4_0, Q4_K, Q5_K, Q6_K])
+@pytest.mark.parametrize("batch", [9, 16, 33, 64])
+def test_batch_above_eight(fmt, batch):
+    # groups of 8 activation rows, the last one partial
+    _check(fmt, 45, 512 if fmt in (Q8_0, Q4_0) else 768, batch, 3500 + fmt + batch)
+
+
+def test_batch_32_full_size_headline_shape():
+    case = synth.GEMV_CASES["q4_k_4096x4096"]
+    W, X = synth.gemv_inputs(case, 32)
+    Y = run_gemv(case.fmt, W, case.rows, case.cols, X)
+    idx = _sample_rows(case.rows, 300, 77)
+    Yr, A = oracle.gemv(case.fmt, W, case.rows, case.cols, X, row_idx=idx)
+    assert_agree(Y[:, idx], Yr, A, "q4_k 4096x4096 b32 (sampled rows)")
+
+
 @pytest.mark.parametrize("fmt,cols,batch,offset", [
     (Q5_K, 4096, 8, 0), (Q4_0, 14336, 4, 2), (Q8_0, 12320, 8, 2), (Q6_K, 6144, 5, 0),
     (Q4_K, 8448, 3, 2),
