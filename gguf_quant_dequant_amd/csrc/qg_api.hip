@@ -43,6 +43,13 @@ using namespace qg;
 // Block formats at batch >= QG_MX_MIN_BATCH run on the matrix cores when the
 // activation image and the stage buffers fit in LDS (0 disables).  At batch
 // 1 the VALU kernels are as fast or faster on the measured shapes.
+// Rows per row group and iteration in the MoE gate/up and down kernels.
+#ifndef QG_MOE_GU_U
+#define QG_MOE_GU_U 2
+#endif
+#ifndef QG_MOE_DN_U
+#define QG_MOE_DN_U 2
+#endif
 #ifndef QG_MX_MIN_BATCH
 #define QG_MX_MIN_BATCH 2
 #endif
@@ -581,7 +588,7 @@ int moe_cpt(int fmt) {
 
 template <class F>
 int launch_gateup(MoeParams p, hipStream_t st) {
-    constexpr int U = 2;
+    constexpr int U = QG_MOE_GU_U;
     Shape s;
     p.gu_tiles = p.H / F::CPT;
     if (!shape_for(p.gu_tiles, &s))
@@ -602,7 +609,7 @@ int launch_gateup(MoeParams p, hipStream_t st) {
 
 template <class F>
 int launch_down(MoeParams p, hipStream_t st) {
-    constexpr int U = 2;
+    constexpr int U = QG_MOE_DN_U;
     Shape s;
     p.dn_tiles_per_slot = p.F / F::CPT;
     p.dn_tiles = p.K * p.dn_tiles_per_slot;

@@ -24,6 +24,12 @@
 
 #include "qg_formats.hpp"
 
+// Cache policy of the router rows (read once per token, whole lines per
+// wave instruction).
+#ifndef QG_ROUTER_AUX
+#define QG_ROUTER_AUX 0
+#endif
+
 namespace qg {
 
 struct GemvParams {
@@ -563,7 +569,7 @@ __global__ void __launch_bounds__(64) moe_router_kernel(const float *__restrict_
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int c = c0 + 256 * i + 4 * lane;
-            load_dw<4>(rr, 4u * c, a[i]);
+            load_dw<4, QG_ROUTER_AUX>(rr, 4u * c, a[i]);
             load_dw<4>(rx, 4u * c, b[i]);
         }
 #pragma unroll
