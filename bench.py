@@ -284,6 +284,45 @@ def cpu_baseline(seconds):
                       f"(f64 dequantise-and-dot, one thread, {platform.processor() or 'host'})"}
 
 
+def _oracle_rows(args):
+    import oracle
+    import synth
+    lo, hi, seconds = args
+    case = synth.GEMV_CASES["q4_k_4096x4096"]
+    W, X = synth.gemv_inputs(case, 1)
+    idx = np.arange(lo, hi, dtype=np.int64)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.gemv(case.fmt, W, case.rows, case.cols, X, row_idx=idx)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return n * (hi - lo), el
+
+
+def cpu_baseline_all_cores(seconds):
+    """The same oracle on every host core: one process per core, each running
+    the single-threaded oracle over its own contiguous row range of the
+    headline matrix (the oracle itself is unchanged)."""
+    import multiprocessing as mp
+    import synth
+    case = synth.GEMV_CASES["q4_k_4096x4096"]
+    cores = min(os.cpu_count() or 1, 16)
+    bounds = np.linspace(0, case.rows, cores + 1).astype(int)
+    ctx = mp.get_context("fork")
+    with ctx.Pool(cores) as pool:
+        done = pool.map(_oracle_rows, [(int(bounds[i]), int(bounds[i + 1]), seconds)
+                                       for i in range(cores)])
+    row_bytes = (case.cols // 256) * 144
+    # the processes run side by side: the aggregate rate is the sum of theirs
+    gbs = sum(n * row_bytes / el for n, el in done) / 1e9
+    rows = sum(n for n, _ in done)
+    return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{rows} rows of Q4_K 4096x4096 batch-1 GEMVs, {cores} processes side by "
+                      f"side for ~{seconds:.0f} s each, every one the single-threaded oracle over "
+                      f"its own rows"}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -335,7 +374,9 @@ def main():
                 wall_gbs=round(steps * w.wbytes / wall / 1e9, 1),
                 event_us_per_launch=round(per_us, 3),
                 event_gbs=round(w.wbytes / (per_us * 1e-6) / 1e9, 1),
-                event_frac_hbm=round(w.wbytes / (per_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 3))
+                event_frac_hbm=round(w.wbytes / (per_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+                # multiply-adds of the product, as TFLOP/s (2 flops each)
+                tflops=round(2.0 * case.rows * case.cols * b / (per_us * 1e-6) / 1e12, 2))
             del w
             torch.cuda.empty_cache()
         if not only or "moe_ffn_qwen3_30b_a3b" in only:
@@ -417,6 +458,7 @@ def main():
         del src, dst
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+        line["cpu_baseline_all_cores"] = cpu_baseline_all_cores(args.cpu_seconds / 2)
     print(json.dumps(line), flush=True)
 
 
