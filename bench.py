@@ -309,7 +309,8 @@ def cpu_baseline_all_cores(seconds):
     case = synth.GEMV_CASES["q4_k_4096x4096"]
     cores = min(os.cpu_count() or 1, 16)
     bounds = np.linspace(0, case.rows, cores + 1).astype(int)
-    ctx = mp.get_context("fork")
+    # fresh interpreters that import the oracle only (no GPU runtime)
+    ctx = mp.get_context("spawn")
     with ctx.Pool(cores) as pool:
         done = pool.map(_oracle_rows, [(int(bounds[i]), int(bounds[i + 1]), seconds)
                                        for i in range(cores)])
