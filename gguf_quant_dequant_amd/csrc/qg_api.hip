@@ -233,6 +233,12 @@ int launch_gemv(GemvParams p, hipStream_t st) {
         return fail(QG_EUNSUPPORTED, "qgemv: %u columns need %d lane tiles per row at batch %d; "
                                      "at most 512 are supported",
                     p.cols, p.tiles, B);
+    // Batch 1 with one wave per row (64-lane groups): workgroups of two
+    // waves, twice as many of them (Q4_K 4096 x 4096: 5.48 -> 5.39 us).
+    if (B == 1 && s.S == 1 && s.lpr == 64) {
+        s.G = 2;
+        s.threads = 128;
+    }
     p.lpr = s.lpr;
     p.S = s.S;
     p.G = s.G;
@@ -798,6 +804,13 @@ int moe_ffn_impl(const char *who, const float *x, const float *residual, float *
         return fail(QG_EUNSUPPORTED, "%s: sizes do not tile", who);
     if (hidden / moe_cpt(gate_fmt) > 512 || top_k * (expert_dim / moe_cpt(down_fmt)) > 512)
         return fail(QG_EUNSUPPORTED, "%s: hidden or top_k * expert_dim too large", who);
+    // several tokens: the gate/up tiles are the batch-4 GEMV's
+    if (tokens > 1) {
+        const int cpt4 = gemv_cpt(gate_fmt, 4, hidden);
+        if (cpt4 == 0 || hidden % cpt4 != 0 || hidden / cpt4 > 512)
+            return fail(QG_EUNSUPPORTED, "%s: hidden %lld too wide for several tokens", who,
+                        (long long)hidden);
+    }
 
     uint8_t *ws = (uint8_t *)workspace;
     MoeParams p{};
