@@ -50,6 +50,14 @@ using namespace qg;
 #ifndef QG_MOE_DN_U
 #define QG_MOE_DN_U 2
 #endif
+// 1: workgroups of half the threads (half the row groups) in the MoE
+// gate/up or down kernel.
+#ifndef QG_MOE_GU_T128
+#define QG_MOE_GU_T128 0
+#endif
+#ifndef QG_MOE_DN_T128
+#define QG_MOE_DN_T128 0
+#endif
 #ifndef QG_MX_MIN_BATCH
 #define QG_MX_MIN_BATCH 2
 #endif
@@ -599,6 +607,10 @@ int launch_gateup(MoeParams p, hipStream_t st) {
     p.gu_tiles = p.H / F::CPT;
     if (!shape_for(p.gu_tiles, &s))
         return fail(QG_EUNSUPPORTED, "moe_ffn: hidden %d too wide for the gate/up kernel", p.H);
+    if (QG_MOE_GU_T128 && s.S == 1 && s.G >= 2) {
+        s.G /= 2;
+        s.threads = 128;
+    }
     p.gu_lpr = s.lpr;
     p.gu_S = s.S;
     p.gu_G = s.G;
@@ -621,6 +633,10 @@ int launch_down(MoeParams p, hipStream_t st) {
     p.dn_tiles = p.K * p.dn_tiles_per_slot;
     if (!shape_for(p.dn_tiles, &s))
         return fail(QG_EUNSUPPORTED, "moe_ffn: top_k * expert_dim too wide for the down kernel");
+    if (QG_MOE_DN_T128 && s.S * s.G * 64 > 128 && s.G >= 2) {
+        s.G /= 2;
+        s.threads /= 2;
+    }
     p.dn_lpr = s.lpr;
     p.dn_S = s.S;
     p.dn_G = s.G;
