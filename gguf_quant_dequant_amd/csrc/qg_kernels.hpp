@@ -864,8 +864,9 @@ __global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
 // moe_ffn_tokens: T <= 8 decode tokens, each routed on its own (the
 // aprender-serve page's moe_layer per token), with the expert GEMVs grouped
 // by expert so that every selected expert's gate and up rows are read once
-// for all the tokens that chose it (the batch semantics of the
-// weight_matrix.rs page's apply_batch, applied per expert).
+// for all the tokens of a group that chose it (the batch semantics of the
+// weight_matrix.rs page's apply_batch, applied per expert).  The host runs
+// the gate/up kernel once per group of up to four tokens.
 
 // logits[t][e] = sum_i R[e][i] * x[t][i] in f64: one wave per expert; the
 // router row is read once for all T tokens.
@@ -934,11 +935,11 @@ __device__ __forceinline__ int distinct_experts(const int *s_sel, int nroutes, i
     return __popcll(m);
 }
 
-// Routing of all T tokens (wave t routes token t), the distinct-expert
-// table, then row tasks (distinct expert u, row j): the gate and up rows of
-// expert s_uexp[u] are read once and dotted with the B activation vectors
-// (tokens past T are zero), and every token t that chose the expert in slot
-// s gets act[t][s][j] = w[t][s] * silu(g_t) * u_t.
+// Routing of the group's T tokens (wave w routes tokens w, w + waves, ...),
+// the distinct-expert table, then row tasks (distinct expert u, row j): the
+// gate and up rows of expert s_uexp[u] are read once and dotted with the B
+// activation vectors (tokens past T are zero), and every token t that chose
+// the expert in slot s gets act[t][s][j] = w[t][s] * silu(g_t) * u_t.
 template <class F, int B, int U>
 __global__ void __launch_bounds__(512) moe_gateup_tokens_kernel(MoeParams p) {
     __shared__ int s_sel[kMaxRoutes];

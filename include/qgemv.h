@@ -211,11 +211,11 @@ size_t moe_ffn_tokens_workspace_bytes(int64_t tokens, int64_t n_experts,
  *   y[t] = residual[t] + sum_s down[e_{t,s}] a[t][s]   for t < T,
  *
  * with every quantity as moe_ffn defines it for token t.  The expert GEMVs
- * are grouped by expert: the gate and up rows of every expert that any
- * token selected are read once and dotted with the activations of all T
- * tokens (weight_matrix.rs apply_batch semantics), and each token that
- * chose the expert receives its own SwiGLU activation.  The down GEMVs run
- * per token.
+ * are grouped by expert: within each group of up to four tokens, the gate
+ * and up rows of every expert that a token of the group selected are read
+ * once and dotted with the group's activations (weight_matrix.rs
+ * apply_batch semantics), and each token that chose the expert receives
+ * its own SwiGLU activation.  The down GEMVs run per token.
  *
  *   x, residual, y  float [T][H]; y may alias residual, not x.
  *   tokens       T, 1..8, with T * top_k <= 64.
