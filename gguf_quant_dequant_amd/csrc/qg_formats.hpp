@@ -70,13 +70,15 @@ __device__ __forceinline__ void prep_f32(const float (&x)[B][F::CPT],
 
 // Activation tile as base-256 digits, for exact integer dot products.
 // Each run of RUNLEN columns gets its own power-of-two scale 2^s, chosen so
-// that the largest |x| * 2^s lies in [2^20, 2^21).  X = x * 2^s, taken to
-// an integer within one unit, is split into digits X = 65536 p2 + 256 p1 +
-// p0 with p0, p1 in [-128, 127] and |p2| <= 33.  Plane k holds digit k of
-// four consecutive columns per dword (column c in byte c % 4), so v_dot4 of
-// four int8 codes with a plane dword is an exact partial sum.  f = 2^-s, or
-// NaN when the run holds a non-finite value.  The rounding of X bounds the
-// error of a product sum by 2^-20 of sum |code| * max|x| over the run.
+// that the largest |x| * 2^s lies in [2^21, 2^22).  X = rint(x * 2^s) (the
+// scaling is exact, the rounding is to nearest, so |X - x 2^s| <= 1/2) is
+// split into digits X = 65536 p2 + 256 p1 + p0 with p0, p1 in [-128, 127]
+// and |p2| <= 64.  Plane k holds digit k of four consecutive columns per
+// dword (column c in byte c % 4), so v_dot4 of four int8 codes with a plane
+// dword is an exact partial sum.  f = 2^-s, or NaN when the run holds a
+// non-finite value.  Error: every activation is represented to within
+// 2^-s / 2 <= 2^-22 max|x| of the run, so a run's product sum is off by at
+// most 2^-22 * max|x| * sum |w| over the run (w the dequantised weights).
 template <int CPT, int NRUN, int B>
 struct XI8 {
     uint32_t p[B][3][CPT / 4];
@@ -93,7 +95,7 @@ __device__ __forceinline__ void digits_run(const float *x, uint32_t *p0, uint32_
         mb = a > mb ? a : mb;
     }
     // frexp exponent e: max in [2^(e-1), 2^e); 0 for a zero maximum
-    int s = 21 - __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, mb));
+    int s = 22 - __builtin_amdgcn_frexp_expf(__builtin_bit_cast(float, mb));
     s = s > 126 ? 126 : s;
     const float up = __builtin_bit_cast(float, (uint32_t)(s + 127) << 23);
     *f = mb < 0x7F800000u ? __builtin_bit_cast(float, (uint32_t)(127 - s) << 23)
@@ -104,7 +106,8 @@ __device__ __forceinline__ void digits_run(const float *x, uint32_t *p0, uint32_
         // byte 2 (sign-extended) is p2
         uint32_t y[4];
 #pragma unroll
-        for (int i = 0; i < 4; i++) y[i] = (uint32_t)(int)fmaf(x[4 * q + i], up, 32896.0f);
+        for (int i = 0; i < 4; i++)
+            y[i] = (uint32_t)((int)__builtin_rintf(x[4 * q + i] * up) + 32896);
         const uint32_t a = __builtin_amdgcn_perm(y[1], y[0], 0x05040100u);
         const uint32_t b = __builtin_amdgcn_perm(y[3], y[2], 0x05040100u);
         p0[q] = __builtin_amdgcn_perm(b, a, 0x06040200u) ^ 0x80808080u;

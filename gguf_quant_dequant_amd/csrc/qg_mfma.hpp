@@ -2,20 +2,24 @@
 // cores: v_mfma_f32_32x32x16_f16 with the weight codes as one operand and
 // the activations as the other.
 //
-// Numbers.  A weight code n (an unsigned integer below 1024) is widened to
-// 16 bits and used as an IEEE binary16 bit pattern, i.e. the subnormal
-// n * 2^-24, which the matrix core multiplies exactly.  Signed codes are
-// made unsigned by an offset (Q6_K's q is already 0..63 with value q - 32;
-// Q8_0's int8 is flipped to q + 128; Q4_0's nibble is 0..15 with value
-// q - 8).  Each 256-column chunk of each activation row is scaled by a power
-// of two 2^e, chosen so its largest magnitude lies in [2^13, 2^14), and
-// split into hi = RTZ_f16(x') and lo = RTZ_f16(x' - hi), so that
+// Numbers.  Codes enter the matrix core as exact f16 values.  Unsigned
+// K-quant codes n (< 256) are widened to 16 bits and used as an IEEE
+// binary16 bit pattern, i.e. the subnormal n * 2^-24, which the matrix core
+// multiplies exactly.  Codes with a zero point (Q6_K's q - 32, Q8_0's signed
+// q, Q4_0's q - 8) are turned into the signed integers themselves: the code
+// byte u (an unsigned 0..255 form) becomes the low byte of the f16 pattern
+// 0x64uu = 1024 + u, and a packed f16 subtraction of 1024 + offset leaves
+// u - offset, exactly (every integer up to 2048 is an f16 value).  A code at
+// its zero point is therefore an exact 0 and contributes nothing.  Each
+// 256-column chunk of each activation row is scaled by a power of two 2^e,
+// chosen so its largest magnitude lies in [2^13, 2^14), and split into
+// hi = RTZ_f16(x') and lo = RTZ_f16(x' - hi), so that
 // |x' - hi - lo| < 2^-21 |x'|.  The matrix core sums code * hi and
-// code * lo over 16 columns in f32; the accumulator starts at
-// -offset * 2^-24 * sum(x') over the code group, so the sum is that of
-// (code - offset) * x' * 2^-24.  The group's scale (d * sc, with the K-quant
-// min term d_min * m * sum(x') applied beside it) multiplies the group sum in
-// f32, and 2^(24 - e) takes each chunk back to the activations' units.
+// code * lo over 16 columns in f32.  The group's scale (d * sc; for the
+// signed codes times 2^-24, for the K-quants the min term d_min * m *
+// sum(x') is carried beside it as an accumulator seed -sum(x') * 2^-24)
+// multiplies the group sum in f32, and 2^(24 - e) takes each chunk back to
+// the activations' units.
 //
 // Work layout.  A tile is 32 consecutive weight rows (the MFMA's n); lane l
 // of a wave feeds row l % 32 and the half kh = l / 32 of each 16-column
@@ -78,6 +82,27 @@ __device__ __forceinline__ u32x4 widen2(uint32_t c0, uint32_t c1) {
     return r;
 }
 
+typedef _Float16 half2 __attribute__((ext_vector_type(2)));
+
+// Eight code bytes u (two dwords) -> eight f16 lanes holding the integers
+// u - OFF, in byte order: v_perm_b32 pairs each byte with 0x64 (the f16
+// 1024 + u), then one packed f16 subtraction of 1024 + OFF per two codes.
+// Both steps are exact for u < 256 and OFF <= 255.
+template <int OFF>
+__device__ __forceinline__ u32x4 widen2s(uint32_t c0, uint32_t c1) {
+    constexpr uint32_t kHi = 0x64646464u;
+    const half2 sub = {(_Float16)(-(1024 + OFF)), (_Float16)(-(1024 + OFF))};
+    u32x4 r;
+    r[0] = __builtin_amdgcn_perm(kHi, c0, 0x04010400u);
+    r[1] = __builtin_amdgcn_perm(kHi, c0, 0x04030402u);
+    r[2] = __builtin_amdgcn_perm(kHi, c1, 0x04010400u);
+    r[3] = __builtin_amdgcn_perm(kHi, c1, 0x04030402u);
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+        r[i] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(half2, (uint32_t)r[i]) + sub);
+    return r;
+}
+
 template <int S>
 __device__ __forceinline__ uint32_t shl(uint32_t v) {
     if constexpr (S >= 0) return v << S;
@@ -103,10 +128,11 @@ __device__ __forceinline__ float group_max(float v) {
 // Builds the activation image of all nc chunks in LDS (ximg), one wave per
 // (chunk, batch row).  Batch row b starts at float b * xstride of X (X may
 // be a column slice of a wider activation matrix; xbytes bounds the reads).
-// coff = -offset * 2^-24 of the weight format; glanes = lanes per code
-// group (4 for 16-column groups, 8 for 32).  Batch rows >= batch and
-// columns >= cols read as zero.
-template <int B>
+// With SEEDS (the K-quants) each code group's accumulator seed
+// coff * sum(x') is stored beside the operands (coff = -2^-24, the min
+// term); glanes = lanes per code group (4 for 16-column groups, 8 for 32).
+// Batch rows >= batch and columns >= cols read as zero.
+template <int B, bool SEEDS>
 __device__ void build_ximg(const float *__restrict__ X, uint32_t cols, uint32_t xstride,
                            uint32_t xbytes, int batch, int nc, float coff, int glanes,
                            uint8_t *ximg) {
@@ -152,12 +178,14 @@ __device__ void build_ximg(const float *__restrict__ X, uint32_t cols, uint32_t 
         lv[1] = __builtin_bit_cast(uint32_t, l23);
         *(u32x2 *)(rec + 2 * ((g * 2 * B + b) * 16 + pos)) = hv;
         *(u32x2 *)(rec + 2 * ((g * 2 * B + B + b) * 16 + pos)) = lv;
-        float s = (xs[0] + xs[1]) + (xs[2] + xs[3]);
-        s = glanes == 8 ? group_sum<8>(s) : group_sum<4>(s);
-        if ((lane & (glanes - 1)) == 0) {
-            float *cp = (float *)(rec + ximg_a(B)) + (g * KH + b / 4) * 8;
-            cp[b & 3] = coff * s;
-            cp[4 + (b & 3)] = 0.f;
+        if constexpr (SEEDS) {
+            float s = (xs[0] + xs[1]) + (xs[2] + xs[3]);
+            s = glanes == 8 ? group_sum<8>(s) : group_sum<4>(s);
+            if ((lane & (glanes - 1)) == 0) {
+                float *cp = (float *)(rec + ximg_a(B)) + (g * KH + b / 4) * 8;
+                cp[b & 3] = coff * s;
+                cp[4 + (b & 3)] = 0.f;
+            }
         }
         if (lane == 0)
             ((float *)(rec + ximg_a(B) + ximg_c(B)))[4 * (b / 4) + (b & 3)] =
@@ -191,8 +219,8 @@ __device__ __forceinline__ u32x4 a_op(const uint8_t *rec, const XLane &xl, int g
     return *(const u32x4 *)(rec + xl.a + 64 * B * g);
 }
 
-// Seeds (-offset * 2^-24 * sum(x') of the code group starting at
-// sub-group g) of this lane's batch rows.
+// Seeds (-2^-24 * sum(x') of the code group starting at sub-group g, the
+// K-quant min term) of this lane's batch rows.
 template <int B>
 __device__ __forceinline__ f32x4 c_vals(const uint8_t *rec, const XLane &xl, int g) {
     return *(const f32x4 *)(rec + xl.c + 32 * kh_of(B) * g);
@@ -256,9 +284,10 @@ __device__ __forceinline__ RowRd<RA> make_rowrd(const uint8_t *row, uint32_t del
 //
 // Each format decodes halves h0 .. h1 - 1 (of two) of one 256-column chunk
 // of its lane's row and adds, for each of the lane's NB batch rows, the sum
-// over those columns of weight * x' * 2^-24 into r.  CHUNK = bytes per chunk, SC = 16-byte units per row slot
-// (odd, which spreads the rows over LDS banks), GW = code-group width,
-// OFF = code offset.
+// over those columns of weight * x' * 2^-24 into r.  CHUNK = bytes per
+// chunk, SC = 16-byte units per row slot (odd, which spreads the rows over
+// LDS banks), GW = code-group width, SEEDS = the image carries per-group
+// accumulator seeds (the K-quant min term).
 
 // Q6_K (web page: docs.rs, crate ferrox-cuda 0.14.0, source src/gpu.rs,
 // Q6_K_MATVEC_KERNEL_SRC): 210-byte blocks, ql[128] at 0, qh[64] at 128,
@@ -268,7 +297,7 @@ __device__ __forceinline__ RowRd<RA> make_rowrd(const uint8_t *row, uint32_t del
 // holds l = 16u .. 16u+15 of quarter t.
 struct MQ6K {
     static constexpr int CHUNK = 210, SC = 15, GW = 16;
-    static constexpr float OFF = 32.f;
+    static constexpr bool SEEDS = false;
 
     template <int B, bool RA>
     static __device__ __forceinline__ void chunk(const RowRd<RA> &rd, const uint8_t *rec,
@@ -278,7 +307,7 @@ struct MQ6K {
         uint32_t S[4];
 #pragma unroll
         for (int j = 0; j < 4; j++) S[j] = rd.dw(192 + 4 * j);
-        const float d = f16_lo(rd.dw(208));
+        const float d = f16_lo(rd.dw(208)) * 0x1p-24f;  // codes are integers q - 32
         const f32x16 z = {};
 #pragma unroll
         for (int h = 0; h < 2; h++) {
@@ -302,12 +331,12 @@ struct MQ6K {
 #pragma unroll
                     for (int half = 0; half < 2; half++) {
                         const int G = 8 * h + 2 * (pp + 2 * half) + u;
-                        const u32x4 bw = half ? widen2(ch[0], ch[1]) : widen2(cl[0], cl[1]);
+                        const u32x4 bw =
+                            half ? widen2s<32>(ch[0], ch[1]) : widen2s<32>(cl[0], cl[1]);
                         const f32x16 D = mfma(a_op<B>(rec, xl, G), bw, z);
-                        const f32x4 sd = c_vals<B>(rec, xl, G);
                         const float s = d * sbyte_at(S[G >> 2], G & 3);
 #pragma unroll
-                        for (int i = 0; i < NB; i++) r[i] = fmaf(s, (D[i] + D[4 + i]) + sd[i], r[i]);
+                        for (int i = 0; i < NB; i++) r[i] = fmaf(s, D[i] + D[4 + i], r[i]);
                     }
                 }
             }
@@ -324,7 +353,7 @@ struct MQ6K {
 template <bool FIVE>
 struct MK45 {
     static constexpr int CHUNK = FIVE ? 176 : 144, SC = FIVE ? 13 : 11, GW = 32;
-    static constexpr float OFF = 1.f;  // seeds hold -sum(x') * 2^-24 for the min term
+    static constexpr bool SEEDS = true;  // seeds hold -sum(x') * 2^-24 for the min term
     static constexpr int QS = FIVE ? 48 : 16;
 
     template <int B, bool RA>
@@ -398,9 +427,10 @@ struct MK45 {
 // Q8_0 (same page, Q8_0_MATVEC_KERNEL_SRC): 34-byte blocks of 32 columns,
 // f16 d at 0, int8 codes at 2; value d * q.  Eight blocks per chunk (fewer
 // in a row's last chunk when the row is not a multiple of 256 columns).
+// The int8 q is flipped to q + 128 and widened back to the integer q.
 struct MQ80 {
     static constexpr int CHUNK = 272, SC = 19, GW = 32;
-    static constexpr float OFF = 128.f;
+    static constexpr bool SEEDS = false;
 
     template <int B, bool RA>
     static __device__ __forceinline__ void chunk(const RowRd<RA> &rd, const uint8_t *rec,
@@ -411,19 +441,18 @@ struct MQ80 {
 #pragma unroll
         for (int blk = 0; blk < 8; blk++) {
             if (blk < nblk && blk >= 4 * h0 && blk < 4 * h1) {
-                const float d = f16_lo(rd.dw(34 * blk));
+                const float d = f16_lo(rd.dw(34 * blk)) * 0x1p-24f;
                 f32x16 D;
 #pragma unroll
                 for (int j = 0; j < 2; j++) {
                     uint32_t A[2];
                     rd.piece(34 * blk + 2 + 16 * j, A);
-                    const u32x4 bw = widen2(A[0] ^ 0x80808080u, A[1] ^ 0x80808080u);
+                    const u32x4 bw = widen2s<128>(A[0] ^ 0x80808080u, A[1] ^ 0x80808080u);
                     const int g = 2 * blk + j;
                     D = mfma(a_op<B>(rec, xl, g), bw, j ? D : z);
                 }
-                const f32x4 sd = c_vals<B>(rec, xl, 2 * blk);
 #pragma unroll
-                for (int i = 0; i < NB; i++) r[i] = fmaf(d, (D[i] + D[4 + i]) + sd[i], r[i]);
+                for (int i = 0; i < NB; i++) r[i] = fmaf(d, D[i] + D[4 + i], r[i]);
             }
         }
     }
@@ -434,7 +463,7 @@ struct MQ80 {
 // element j + 16 the high nibble; value d * (q - 8).
 struct MQ40 {
     static constexpr int CHUNK = 144, SC = 11, GW = 32;
-    static constexpr float OFF = 8.f;
+    static constexpr bool SEEDS = false;
 
     template <int B, bool RA>
     static __device__ __forceinline__ void chunk(const RowRd<RA> &rd, const uint8_t *rec,
@@ -445,17 +474,16 @@ struct MQ40 {
 #pragma unroll
         for (int blk = 0; blk < 8; blk++) {
             if (blk < nblk && blk >= 4 * h0 && blk < 4 * h1) {
-                const float d = f16_lo(rd.dw(18 * blk));
+                const float d = f16_lo(rd.dw(18 * blk)) * 0x1p-24f;
                 uint32_t A[2];
                 rd.piece(18 * blk + 2, A);
                 const int g = 2 * blk;
                 f32x16 D = mfma(a_op<B>(rec, xl, g),
-                                widen2(A[0] & 0x0F0F0F0Fu, A[1] & 0x0F0F0F0Fu), z);
+                                widen2s<8>(A[0] & 0x0F0F0F0Fu, A[1] & 0x0F0F0F0Fu), z);
                 D = mfma(a_op<B>(rec, xl, g + 1),
-                         widen2((A[0] >> 4) & 0x0F0F0F0Fu, (A[1] >> 4) & 0x0F0F0F0Fu), D);
-                const f32x4 sd = c_vals<B>(rec, xl, g);
+                         widen2s<8>((A[0] >> 4) & 0x0F0F0F0Fu, (A[1] >> 4) & 0x0F0F0F0Fu), D);
 #pragma unroll
-                for (int i = 0; i < NB; i++) r[i] = fmaf(d, (D[i] + D[4 + i]) + sd[i], r[i]);
+                for (int i = 0; i < NB; i++) r[i] = fmaf(d, D[i] + D[4 + i], r[i]);
             }
         }
     }
@@ -498,7 +526,7 @@ struct MxParams {
     int32_t nu;           // 16-byte units copied per row segment
     int32_t nbuf;         // stage buffers (1 or 2)
     int32_t last_nblk;    // 32-column blocks in a row's last chunk (block formats)
-    float coff;           // -OFF * 2^-24
+    float coff;           // seed factor of the K-quant min term: -2^-24
     // column slices: W and X point at the slice's first column, rows keep
     // their full strides; the slice's sums are added to Y when accumulate
     uint32_t x_stride;    // floats between batch rows of X
@@ -567,9 +595,11 @@ __global__ void __launch_bounds__(512) qgemv_mx_kernel(MxParams p) {
     // activations; a streaming one converts the activations first.
     if (p.nbuf == 1) {
         if (ns > 0) issue(0);
-        build_ximg<B>(p.X, p.cols, p.x_stride, p.x_bytes, p.batch, p.nc, p.coff, F::GW / 4, smem);
+        build_ximg<B, F::SEEDS>(p.X, p.cols, p.x_stride, p.x_bytes, p.batch, p.nc, p.coff,
+                                F::GW / 4, smem);
     } else {
-        build_ximg<B>(p.X, p.cols, p.x_stride, p.x_bytes, p.batch, p.nc, p.coff, F::GW / 4, smem);
+        build_ximg<B, F::SEEDS>(p.X, p.cols, p.x_stride, p.x_bytes, p.batch, p.nc, p.coff,
+                                F::GW / 4, smem);
         if (ns > 0) issue(0);
     }
     const XLane xl = make_xlane<B>(lane);

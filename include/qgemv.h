@@ -115,12 +115,19 @@ const char *qg_last_error(void);
  *
  * Dequantisation per element follows the block layouts of the gpu.rs page
  * kernels.  At batch 1 products are formed and accumulated in f32 on the
- * vector ALUs and reduced across lanes with a fixed tree.  At batch >= 2
- * (and for batch-1 rows wider than 512 lane tiles) the block formats run
- * on the matrix cores: codes are exact f16 values, each 256-column chunk of
- * X is split into f16 hi + lo parts after a power-of-two scaling (relative
- * error < 2^-21 per element), sums are f32.  Results are deterministic run
- * to run.  Limits: rows < 2^31, cols <= 65536; rows that fit neither
+ * vector ALUs and reduced across lanes with a fixed tree; Q6_K is the
+ * exception: its codes meet the activations in exact int32 dot products,
+ * each run of 16 activation columns represented as integers X = rint(x *
+ * 2^s) with max|X| in [2^21, 2^22), so a run's product sum is off by at
+ * most 2^-22 * max|x| * sum|w| over the run (within the tolerance
+ * 1e-4 * sum|w x| unless a run's largest |x| exceeds its typical |x| by
+ * more than ~400x where the weights meet the large values with small
+ * codes).  At batch >= 2 (and for batch-1 rows wider than 512 lane tiles)
+ * the block formats run on the matrix cores: codes are exact f16 values
+ * (codes at a format's zero point are exact zeros), each 256-column chunk
+ * of X is split into f16 hi + lo parts after a power-of-two scaling
+ * (relative error < 2^-21 per element), sums are f32.  Results are
+ * deterministic run to run.  Limits: rows < 2^31, cols <= 65536; rows that fit neither
  * kernel (e.g. more than ~64 chunks of 256 columns at batch 1 beyond 512
  * lane tiles) return QG_EUNSUPPORTED.  Allocates nothing.
  */

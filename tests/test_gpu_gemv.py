@@ -155,14 +155,11 @@ def test_zero_weights_give_zero():
         assert np.array_equal(Y, np.zeros_like(Y))
 
 
-@pytest.mark.parametrize("fmt", [Q8_0, Q4_0, Q6_K])
-def test_codes_at_the_zero_point_give_exact_zero_at_batch_1(fmt):
+def _zero_point_matrix(fmt, rows, cols, seed):
     # nonzero scales with every code at the format's zero point (q = 0,
-    # nibble 8, q = 32): the batch-1 kernels carry the offset exactly
-    rows, cols = 13, 512
-    W = _matrix(fmt, rows, cols, 6200 + fmt)
-    bb = q.qg_block_bytes(fmt)
-    B = W.reshape(-1, bb)
+    # nibble 8, q = 32): every dequantised weight is exactly 0
+    W = _matrix(fmt, rows, cols, seed)
+    B = W.reshape(-1, q.qg_block_bytes(fmt))
     if fmt == Q8_0:
         B[:, 2:34] = 0
     elif fmt == Q4_0:
@@ -170,11 +167,38 @@ def test_codes_at_the_zero_point_give_exact_zero_at_batch_1(fmt):
     else:
         B[:, 0:128] = 0
         B[:, 128:192] = 0xAA
-    X = synth.activations(synth.rng(6201), 1, cols)
+    return W
+
+
+@pytest.mark.parametrize("fmt", [Q8_0, Q4_0, Q6_K])
+@pytest.mark.parametrize("batch", [1, 2, 3, 4, 8, 16])
+def test_codes_at_the_zero_point_give_exact_zero(fmt, batch):
+    # the VALU kernels (batch 1) and the matrix-core kernel (batch >= 2)
+    # carry the code offset exactly: a row of zero weights gives +-0
+    rows, cols = 45, 512
+    W = _zero_point_matrix(fmt, rows, cols, 6200 + fmt)
+    X = synth.activations(synth.rng(6201 + batch), batch, cols)
     Y = run_gemv(fmt, W, rows, cols, X)
     assert np.array_equal(Y, np.zeros_like(Y))
     Yr, A = oracle.gemv(fmt, W, rows, cols, X)
     assert np.array_equal(Yr, np.zeros_like(Yr))
+
+
+@pytest.mark.parametrize("fmt", [Q8_0, Q4_0, Q6_K])
+@pytest.mark.parametrize("batch", [2, 4, 8])
+def test_zero_point_blocks_inside_random_rows(fmt, batch):
+    # every other block of a random matrix at its zero point, large
+    # activations: the zero blocks add nothing on the matrix cores either
+    rows, cols = 70, 2048
+    W = _matrix(fmt, rows, cols, 6300 + fmt)
+    Z = _zero_point_matrix(fmt, rows, cols, 6300 + fmt)
+    bb = q.qg_block_bytes(fmt)
+    Wb, Zb = W.reshape(-1, bb), Z.reshape(-1, bb)
+    Wb[::2] = Zb[::2]
+    X = 1e3 * synth.activations(synth.rng(6301 + batch), batch, cols)
+    Y = run_gemv(fmt, W, rows, cols, X)
+    Yr, A = oracle.gemv(fmt, W, rows, cols, X)
+    assert_agree(Y, Yr, A, f"fmt {fmt} b{batch} half zero-point blocks")
 
 
 def test_q8_0_code_minus_128():
@@ -217,3 +241,39 @@ def test_workload_full_size(name):
             Yr, A = oracle.gemv(case.fmt, W, case.rows, case.cols, X, row_idx=idx)
             assert_agree(Y[:, idx], Yr, A, f"{name} b{batch} (sampled rows)")
             assert np.isfinite(Y).all()
+
+
+def _q6_k_set_zero_point(W, rows, cols, col):
+    # code q = 32 (weight 0) at column col of every row: the low nibble of
+    # ql[64h + 32(t%2) + l] (nibble t/2) and bits 2t..2t+1 of qh[32h + l]
+    rb = q.qg_row_bytes(Q6_K, cols)
+    Wr = W.reshape(rows, rb)
+    sb, e = divmod(int(col), 256)
+    h, t, l = e // 128, (e % 128) // 32, e % 32
+    o = 210 * sb
+    iql = o + 64 * h + 32 * (t % 2) + l
+    nib = 4 * (t // 2)
+    Wr[:, iql] &= np.uint8(0xFF ^ (0xF << nib))
+    iqh = o + 128 + 32 * h + l
+    Wr[:, iqh] = (Wr[:, iqh] & np.uint8(0xFF ^ (0x3 << (2 * t)))) | np.uint8(0x2 << (2 * t))
+
+
+@pytest.mark.parametrize("batch", [1, 4])
+def test_q6_k_outlier_activations(batch):
+    # outlier columns 64x the typical magnitude in a third of the 16-column
+    # runs, with every row's code at the zero point in those columns (the
+    # case where a run's error bound 2^-22 * max|x| * sum|w| is largest
+    # against sum |w x|): inside the tolerance at this dynamic range
+    rows, cols = 96, 4096
+    W = _matrix(Q6_K, rows, cols, 6400 + batch)
+    X = synth.activations(synth.rng(6401 + batch), batch, cols)
+    g = synth.rng(6402 + batch)
+    cols_out = g.choice(cols, size=cols // 48, replace=False)
+    X[:, cols_out] *= 64.0
+    for c in cols_out:
+        _q6_k_set_zero_point(W, rows, cols, c)
+    Wd = oracle.dequant_matrix(Q6_K, W, rows, cols)
+    assert np.all(Wd[:, cols_out] == 0)
+    Y = run_gemv(Q6_K, W, rows, cols, X)
+    Yr, A = oracle.gemv(Q6_K, W, rows, cols, X)
+    assert_agree(Y, Yr, A, f"q6_k outliers b{batch}")

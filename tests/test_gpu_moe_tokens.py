@@ -133,3 +133,32 @@ def test_qwen3_moe_shape_tokens(T):
                   case.top_k, case.hidden, case.expert_dim)
     xs, rs = synth.moe_tokens(case)
     _compare(m, xs[:T], rs[:T], f"qwen3 {T} tokens")
+
+
+def test_qwen3_moe_shape_all_64_tokens_in_calls_of_8():
+    # every token the benchmark routes, eight calls of eight tokens
+    case = synth.MOE_CASE
+    router, gate, up, down = synth.moe_weights(case)
+    m = MoeTokens(router, gate, up, down, case.gate_fmt, case.down_fmt, case.n_experts,
+                  case.top_k, case.hidden, case.expert_dim)
+    xs, rs = synth.moe_tokens(case)
+    for t0 in range(0, xs.shape[0], 8):
+        _compare(m, xs[t0:t0 + 8], rs[t0:t0 + 8], f"qwen3 tokens {t0}..{t0 + 7}")
+
+
+def test_non_finite_token_does_not_reach_other_tokens_logits():
+    # H = 512 is not a multiple of the router's 1024-column round: the
+    # columns past H of token 0 must read as zero, not as token 1's values
+    m, g = _small(q.QG_Q4_K, q.QG_Q6_K, E=8, k=2, H=512, seed=64)
+    x = synth.activations(g, 2, m.H)
+    x[1, 3] = np.inf
+    x[1, 100] = np.nan
+    res = synth.activations(g, 2, m.H)
+    y, sel, w, logits = m.gpu(x, res)
+    r = oracle.moe_ffn(x[0], res[0], m.router, m.gate_fmt, m.gate, m.gate_fmt, m.up, m.down_fmt,
+                       m.down, m.H, m.E, m.k, m.F)
+    assert np.all(np.isfinite(logits[0]))
+    lb = np.abs(m.router.astype(np.float64)) @ np.abs(x[0].astype(np.float64))
+    assert np.all(np.abs(logits[0] - r["logits"]) <= 1e-12 * lb)
+    assert np.array_equal(sel[0], r["sel"])
+    assert_agree(y[0], r["y"], r["bound"], "token 0 beside a non-finite token")

@@ -2,10 +2,15 @@
 products) against the oracle's int8-activation GEMV, which quantises the
 activations the same way and accumulates in f64.
 
-Tolerance per row: 1e-4 * sum |w * x_q| + 1e-6 (the quantised activations
-are identical on both sides; only the order and width of the sums differ).
-The departure from the exact GEMV is checked against the quantisation bound
-sum |w| * d / 2 and reported.
+Two checks on every result:
+
+* against the oracle's int8-activation GEMV, per row
+  1e-4 * sum |w * x_q| + 1e-6 (both sides quantise the activations with the
+  same f32 operations; only the order and width of the sums differ);
+* against the exact GEMV's oracle, which does not depend on how the
+  quantiser is written: per row the departure is at most the quantisation
+  bound sum |w| * d / 2 (d the group scale, taken from the exact
+  activations as max|x| / 127 in f64) plus the exact path's tolerance.
 """
 from __future__ import annotations
 
@@ -34,14 +39,34 @@ def run_q8(fmt, W, rows, cols, x, offset=0):
     return Y.cpu().numpy()
 
 
+def check_exact_bound(fmt, W, rows, cols, x, y, what, row_idx=None):
+    """|y - exact| <= sum_c |w_c| * d(c) / 2 * (1 + 1e-3) + 1e-4 * sum |w x| + 1e-6 per
+    row, with d = max |x| / 127 over the 16-column group (f64), exact from
+    the exact GEMV's oracle.  row_idx: y holds only these rows of W."""
+    x64 = np.asarray(x, np.float64)
+    d = np.max(np.abs(x64.reshape(-1, 16)), axis=1) / 127.0
+    Wsub = W.reshape(rows, -1) if row_idx is None else W.reshape(rows, -1)[row_idx]
+    n = Wsub.shape[0]
+    Wd = oracle.dequant_matrix(fmt, Wsub, n, cols)
+    bound = np.abs(Wd) @ np.repeat(d, 16) / 2
+    Ye, Ae = oracle.gemv(fmt, Wsub, n, cols, x[None].astype(np.float32))
+    err = np.abs(np.asarray(y, np.float64) - Ye[0])
+    ok = err <= bound * (1 + 1e-3) + 1e-4 * Ae[0] + 1e-6
+    assert ok.all(), (what, int((~ok).sum()), float(np.max(err - bound)))
+    return float(np.max(err / np.maximum(bound, 1e-30)))
+
+
 def _check(fmt, rows, cols, seed, offset=0, x=None):
     g = synth.rng(seed)
     W = synth.matrix(g, fmt, rows, cols)
     if x is None:
         x = synth.activations(g, 1, cols)[0]
     y = run_q8(fmt, W, rows, cols, x, offset)
+    what = f"q8act fmt {fmt} {rows}x{cols} off{offset}"
     Yr, A = oracle.gemv_q8act(fmt, W, rows, cols, x[None])
-    assert_agree(y[None], Yr, A, f"q8act fmt {fmt} {rows}x{cols} off{offset}")
+    assert_agree(y[None], Yr, A, what)
+    if np.isfinite(x).all():
+        check_exact_bound(fmt, W, rows, cols, x, y, what)
     return W, x, y
 
 
@@ -58,14 +83,14 @@ def test_weights_two_bytes_past_alignment(fmt):
 
 @pytest.mark.parametrize("fmt", FMTS)
 def test_quantisation_error_within_bound(fmt):
-    # the result departs from the exact GEMV by at most sum |w| * d / 2
+    # larger rows; the ratio of the departure to its bound is reported
     rows, cols = 64, 2048
-    W, x, y = _check(fmt, rows, cols, 900 + fmt)
-    _, d = oracle.quantize_q8(x)
-    Wd = oracle.dequant_matrix(fmt, W, rows, cols)
-    bound = np.abs(Wd) @ np.repeat(d.astype(np.float64), 16) / 2
-    Ye, Ae = oracle.gemv(fmt, W, rows, cols, x[None])
-    assert np.all(np.abs(y - Ye[0]) <= bound * (1 + 1e-3) + 1e-4 * Ae[0] + 1e-6)
+    g = synth.rng(900 + fmt)
+    W = synth.matrix(g, fmt, rows, cols)
+    x = synth.activations(g, 1, cols)[0]
+    y = run_q8(fmt, W, rows, cols, x)
+    ratio = check_exact_bound(fmt, W, rows, cols, x, y, f"bound fmt {fmt}")
+    print(f"\nfmt {fmt}: largest departure / bound = {ratio:.3f}")
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -81,6 +106,8 @@ def test_representable_activations_give_the_exact_result(fmt):
     y = run_q8(fmt, W, rows, cols, x)
     Ye, Ae = oracle.gemv(fmt, W, rows, cols, x[None])
     assert_agree(y[None], Ye, Ae, f"representable fmt {fmt}")
+    Yr, A = oracle.gemv_q8act(fmt, W, rows, cols, x[None])
+    assert_agree(y[None], Yr, A, f"representable fmt {fmt}, int8 oracle")
 
 
 def test_zero_and_non_finite_groups():
@@ -105,6 +132,8 @@ def test_workload_full_size(name):
     sub = W.reshape(case.rows, -1)[idx]
     Yr, A = oracle.gemv_q8act(case.fmt, sub, len(idx), case.cols, X)
     assert_agree(y[None, idx], Yr, A, f"{name} q8act (sampled rows)")
+    check_exact_bound(case.fmt, W, case.rows, case.cols, X[0], y[idx], f"{name} exact bound",
+                      row_idx=idx)
     assert np.isfinite(y).all()
 
 
