@@ -37,6 +37,8 @@ SIGNATURES = {
     "moe_ffn_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_size_t),
     "moe_ffn": ([_P, _P, _P, _P, _INT, _P, _INT, _P, _INT, _P, _I64, _I64, _I64, _I64,
                  _P, _P, _P, ctypes.c_size_t, _P], _INT),
+    "moe_ffn_noalloc": ([_P, _P, _P, _P, _INT, _P, _INT, _P, _INT, _P, _I64, _I64, _I64, _I64,
+                         _P, _P, _P], _INT),
     "qg_route_topk": ([_P, _I64, _I64, _P, _P, _P], _INT),
     "moe_ffn_tokens_workspace_bytes": ([_I64, _I64, _I64, _I64], ctypes.c_size_t),
     "moe_ffn_tokens": ([_P, _P, _P, _P, _INT, _P, _INT, _P, _INT, _P, _I64, _I64, _I64, _I64,
@@ -140,6 +142,17 @@ def moe_ffn(x, residual, y, router, gate_fmt: int, gate, up_fmt: int, up, down_f
                                 _ptr(sel_weights), _ptr(workspace), workspace_bytes,
                                 _stream(stream))
     _check(rc, "moe_ffn")
+
+
+def moe_ffn_noalloc(x, residual, y, router, gate_fmt: int, gate, up_fmt: int, up,
+                    down_fmt: int, down, hidden: int, n_experts: int, top_k: int,
+                    expert_dim: int, sel_experts=None, sel_weights=None, stream=None) -> None:
+    """moe_ffn with the library's own scratch array as its workspace (see include/qgemv.h)."""
+    rc = load_library().moe_ffn_noalloc(_ptr(x), _ptr(residual), _ptr(y), _ptr(router), gate_fmt,
+                                        _ptr(gate), up_fmt, _ptr(up), down_fmt, _ptr(down),
+                                        hidden, n_experts, top_k, expert_dim, _ptr(sel_experts),
+                                        _ptr(sel_weights), _stream(stream))
+    _check(rc, "moe_ffn_noalloc")
 
 
 def qg_route_topk(logits, n_experts: int, top_k: int, sel_experts, sel_weights,

@@ -205,6 +205,25 @@ int moe_ffn(const float *x, const float *residual, float *y,
             int32_t *sel_experts, float *sel_weights, void *workspace,
             size_t workspace_bytes, void *stream);
 
+/*
+ * moe_ffn_noalloc: moe_ffn for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Arguments, semantics, kernels, results and errors are those
+ * of moe_ffn, without the workspace: the library keeps one scratch array
+ * of 1 MiB (1,048,576 bytes) in device memory, per GPU it runs on, for the
+ * life of the process, and uses it as the workspace.  Sizes whose
+ * moe_ffn_workspace_bytes exceed it are refused with QG_EUNSUPPORTED.  The
+ * device current on the calling thread must be the device of `stream`.
+ * Calls no allocating routine.  Every call on one GPU shares that GPU's
+ * array, which keeps the last call's contents (its first E doubles hold the
+ * router logits of the last call): calls that overlap on one GPU race.
+ */
+int moe_ffn_noalloc(const float *x, const float *residual, float *y,
+                    const float *router, int gate_fmt, const void *gate, int up_fmt,
+                    const void *up, int down_fmt, const void *down, int64_t hidden,
+                    int64_t n_experts, int64_t top_k, int64_t expert_dim,
+                    int32_t *sel_experts, float *sel_weights, void *stream);
+
 /* Bytes of caller-owned device workspace moe_ffn_tokens needs for T tokens
  * (f64 logits [T][E], the routes [T][k], the activations [T][k][F]).
  * Returns 0 for invalid sizes. */
