@@ -3,24 +3,30 @@
 
 Prints ONE JSON line.  The headline workload is the Q4_K 4096 x 4096 GEMV at
 batch 1; a step is one qgemv over that matrix.  The other workloads (Q8_0
-256 x 1024, the Q6_K 151936 x 2048 lm_head, the Q5_K / Q4_0 batch sweep and
-the Qwen3-30B-A3B-shaped MoE FFN) are measured in the same run and reported
-under "workloads".
+256 x 1024, the Q6_K 151936 x 2048 lm_head, the Q5_K / Q4_0 batch sweep,
+batches above 8, the int8-activation variant, the Qwen3-30B-A3B-shaped MoE
+FFN, and the plain streaming read that bounds every batch-1 GEMV) are
+measured in the same run and reported under "workloads".
 
-Cold weights: every launch reads a different copy of the weights, and the
-copies together exceed the 256 MB Infinity Cache and the L2s several times
-over, so each launch streams its weights from HBM.  Inputs are resident in
-HBM before the timed region starts.
+Cold weights: consecutive launches read different copies of the weights
+(the copies of a workload cover at least 1 GiB, four times the 256 MB
+Infinity Cache), and right before every timed replay a 1 GiB device copy
+(1 GiB read, 1 GiB written) scrubs the Infinity Cache and the L2s, so every
+timed launch streams its weights from HBM whatever the step count: a copy
+is read again only after at least 1 GiB of other traffic.  Inputs are
+resident in HBM before the timed region starts.
 
 Timing: the K launches of a workload are captured in one HIP graph (the
 host cannot issue launches as fast as the kernels run).  Untimed replays
 come first, for at least --warm-seconds: under sustained load the GPU takes
-a while to reach its steady clocks.  The timed region is one replay of that
-graph, bracketed by torch.cuda.synchronize(): its wall
-time gives the whole-job rate (`value`), and a HIP event pair recorded on the
-replay stream gives the average launch duration behind `roofline`.
-`cpu_baseline` times the C oracle (single thread) on a bounded sample of the
-same workload.
+a while to reach its steady clocks.  Then the scrub, then the timed region:
+one replay of that graph, bracketed by torch.cuda.synchronize().  Its wall
+time gives the whole-job rate (`value`), and a HIP event pair recorded on
+the replay stream gives the average launch duration behind `roofline`.
+The rocprofv3 kernel-trace mean of the same kernel, from the committed
+summary under profiles/ (when it was taken on these kernel sources), is
+printed beside it.  `cpu_baseline` times the C oracle on a bounded sample
+of the same workload.
 """
 from __future__ import annotations
 
@@ -60,19 +66,50 @@ def parse():
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "q4_k_4096x4096_b1_hbm_traffic.md")
-KERNEL_SOURCES = ["qg_api.hip", "qg_kernels.hpp", "qg_formats.hpp", "qg_device.hpp", "qg_mfma.hpp",
-                  "qg_q8act.hpp"]
+TRACE_FILE = os.path.join(ROOT, "profiles", "q4_k_4096x4096_b1_kernel_trace.md")
+CSRC = os.path.join(ROOT, "gguf_quant_dequant_amd", "csrc")
 
 
 def source_digest():
-    """sha256 over the kernel sources, to tell whether counters taken on an
-    earlier build still describe this one."""
+    """sha256 over the kernel sources (every file under csrc/, in name
+    order), to tell whether counters taken on an earlier build still
+    describe this one."""
+    import glob
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "gguf_quant_dequant_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+    for f in sorted(glob.glob(os.path.join(CSRC, "*"))):
+        if f.endswith((".hip", ".hpp")):
+            with open(f, "rb") as fh:
+                h.update(fh.read())
     return h.hexdigest()
+
+
+def _summary_fields(path):
+    """The '- key: value' lines of a committed profile summary."""
+    try:
+        with open(path) as fh:
+            text = fh.read()
+    except OSError:
+        return {}
+    fields = {}
+    for line in text.splitlines():
+        if line.startswith("- ") and ": " in line:
+            k, v = line[2:].split(": ", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    return fields
+
+
+def measured_trace_us():
+    """Mean kernel-trace duration (us) of the headline kernel over the timed
+    replay, from the committed rocprofv3 summary; None when missing or taken
+    on other kernel sources."""
+    f = _summary_fields(TRACE_FILE)
+    if f.get("kernel sources sha256") != source_digest():
+        return None
+    try:
+        return float(f["trace mean dispatch us, timed replay"])
+    except (KeyError, ValueError):
+        return None
 
 
 def measured_traffic():
@@ -80,20 +117,11 @@ def measured_traffic():
     summary (FETCH_SIZE + WRITE_SIZE, each scaled by what the counter reads
     for a copy of known size); None when the summary is missing or was taken
     on other kernel sources."""
-    try:
-        with open(TRAFFIC_FILE) as fh:
-            text = fh.read()
-    except OSError:
-        return None
-    fields = {}
-    for line in text.splitlines():
-        if line.startswith("- ") and ": " in line:
-            k, v = line[2:].split(": ", 1)
-            fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel sources sha256") != source_digest():
+    f = _summary_fields(TRAFFIC_FILE)
+    if f.get("kernel sources sha256") != source_digest():
         return None
     try:
-        return int(fields["HBM bytes per launch"])
+        return int(f["HBM bytes per launch"])
     except (KeyError, ValueError):
         return None
 
@@ -122,6 +150,25 @@ class Gemv:
         else:
             self.q.qgemv(self.case.fmt, W, self.case.rows, self.case.cols, self.X, self.Y,
                          self.batch)
+
+
+class Stream:
+    """The plain streaming read of `nbytes` (qg_stream_read) over rotating
+    cold copies: the floor of any kernel that must read that many bytes."""
+
+    def __init__(self, nbytes, torch, q, grid=0):
+        self.q, self.torch, self.grid = q, torch, grid
+        self.wbytes = nbytes
+        ncopy = max(2, -(-COLD_BYTES // nbytes))
+        first = torch.randint(0, 255, (nbytes,), dtype=torch.uint8, device="cuda")
+        self.copies = [first] + [first.clone() for _ in range(ncopy - 1)]
+        self.out = torch.empty(4096, dtype=torch.int32, device="cuda")
+        self.i = 0
+
+    def launch(self):
+        W = self.copies[self.i % len(self.copies)]
+        self.i += 1
+        self.q.qg_stream_read(W, self.wbytes, self.out, self.grid)
 
 
 class Moe:
@@ -227,13 +274,25 @@ class MoeTokens(Moe):
                               self.w[t:t + T], self.ws, self.wsb)
 
 
-def time_launches(torch, work, steps, warmup, warm_seconds=0.0):
+class Scrub:
+    """A 1 GiB device copy (1 GiB read + 1 GiB written): run right before a
+    timed replay, it evicts the 256 MB Infinity Cache and the L2s."""
+
+    def __init__(self, torch):
+        self.src = torch.ones(COLD_BYTES, dtype=torch.uint8, device="cuda")
+        self.dst = torch.empty_like(self.src)
+
+    def run(self):
+        self.dst.copy_(self.src)
+
+
+def time_launches(torch, work, steps, warmup, warm_seconds=0.0, scrub=None):
     """Capture `steps` back-to-back launches in one HIP graph, replay it
     `warmup` times untimed (and further until `warm_seconds` have passed:
     the GPU reaches its sustained clocks only after some time under load),
-    then time one replay: wall clock between two synchronisations and a HIP
-    event pair on the replay stream.  Returns (wall seconds, event
-    milliseconds)."""
+    scrub the caches, then time one replay: wall clock between two
+    synchronisations and a HIP event pair on the replay stream.  Returns
+    (wall seconds, event milliseconds)."""
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
@@ -252,6 +311,9 @@ def time_launches(torch, work, steps, warmup, warm_seconds=0.0):
     while time.perf_counter() - t_warm < warm_seconds:
         graph.replay()
         torch.cuda.synchronize()
+    if scrub is not None:
+        scrub.run()
+        torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -261,6 +323,24 @@ def time_launches(torch, work, steps, warmup, warm_seconds=0.0):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     return wall, e0.elapsed_time(e1)
+
+
+def host_cpu():
+    """(model name from /proc/cpuinfo, logical CPUs usable by this process)."""
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return model, n
 
 
 def cpu_baseline(seconds):
@@ -279,9 +359,34 @@ def cpu_baseline(seconds):
         if el >= seconds:
             break
     gbs = n * W.nbytes / el / 1e9
+    model, ncpu = host_cpu()
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{n} full Q4_K 4096x4096 batch-1 GEMVs in {el:.1f} s "
-                      f"(f64 dequantise-and-dot, one thread, {platform.processor() or 'host'})"}
+                      f"(f64 dequantise-and-dot, one thread)",
+            "cpu_model": model, "host_logical_cpus": ncpu}
+
+
+def cpu_baseline_moe(seconds):
+    """The oracle (single-threaded C) on the MoE workload: tokens of the
+    Qwen3-30B-A3B-shaped MoE FFN one after another (router, routing, the 8
+    experts' gate / up / down, residual) until `seconds` have passed."""
+    import oracle
+    import synth
+    c = synth.MOE_CASE
+    router, gate, up, down = synth.moe_weights(c)
+    xs, rs = synth.moe_tokens(c)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        t = n % xs.shape[0]
+        oracle.moe_ffn(xs[t], rs[t], router, c.gate_fmt, gate, c.up_fmt, up, c.down_fmt, down,
+                       c.hidden, c.n_experts, c.top_k, c.expert_dim)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(n / el, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n} tokens of the Qwen3-30B-A3B-shaped MoE FFN in {el:.1f} s, one "
+                      f"thread ({el / n * 1e3:.1f} ms per token)"}
 
 
 def _oracle_rows(args):
@@ -300,14 +405,21 @@ def _oracle_rows(args):
             return n * (hi - lo), el
 
 
+# Worker processes for the many-core oracle run: this machine gives one GPU
+# a share of 16 host CPUs, whatever the host's CPU count.
+CPU_SHARE = 16
+
+
 def cpu_baseline_all_cores(seconds):
-    """The same oracle on every host core: one process per core, each running
-    the single-threaded oracle over its own contiguous row range of the
-    headline matrix (the oracle itself is unchanged)."""
+    """The same oracle on the host CPUs this GPU's share allows: one process
+    per CPU (up to 16), each running the single-threaded oracle over its own
+    contiguous row range of the headline matrix (the oracle itself is
+    unchanged)."""
     import multiprocessing as mp
     import synth
     case = synth.GEMV_CASES["q4_k_4096x4096"]
-    cores = min(os.cpu_count() or 1, 16)
+    model, ncpu = host_cpu()
+    cores = max(1, min(ncpu, CPU_SHARE))
     bounds = np.linspace(0, case.rows, cores + 1).astype(int)
     # fresh interpreters that import the oracle only (no GPU runtime)
     ctx = mp.get_context("spawn")
@@ -321,7 +433,30 @@ def cpu_baseline_all_cores(seconds):
     return {"value": round(gbs, 4), "unit": "GB/s", "cores": cores, "kind": "oracle",
             "sample": f"{rows} rows of Q4_K 4096x4096 batch-1 GEMVs, {cores} processes side by "
                       f"side for ~{seconds:.0f} s each, every one the single-threaded oracle over "
-                      f"its own rows"}
+                      f"its own rows ({cores} = min(host logical CPUs {ncpu}, the 16-CPU share "
+                      f"of one GPU on this machine))",
+            "cpu_model": model, "host_logical_cpus": ncpu}
+
+
+# What each workload's kernel computes in (the "dtype" of the line is the
+# headline's).
+ARITH = {
+    "valu_f32": "f32 products and sums on the vector ALUs",
+    "valu_q6k_int": "int8 codes x integer activations (rint at 2^21..2^22 of each 16-column "
+                    "run's max), exact int32 sums, f32 per run",
+    "mfma_f16": "f16 codes x f16 hi + lo activation parts on the matrix cores, f32 sums",
+    "q8act": "int8 codes x int8 activations (per 16 columns), exact int32 sums, f32 per group",
+    "moe": "f64 router, f32 expert GEMVs on the vector ALUs",
+    "read": "plain read, no arithmetic",
+}
+
+
+def gemv_arith(fmt, b, q8):
+    if q8:
+        return ARITH["q8act"]
+    if b == 1:
+        return ARITH["valu_q6k_int"] if fmt == 14 else ARITH["valu_f32"]
+    return ARITH["mfma_f16"]
 
 
 def main():
@@ -337,19 +472,21 @@ def main():
     q.load_library()
     torch.cuda.set_device(0)
     only = set(filter(None, args.only.split(",")))
+    scrub = Scrub(torch)
 
     head_case = synth.GEMV_CASES["q4_k_4096x4096"]
     results = {}
-    head = None
     if not only or "q4_k_4096x4096_b1" in only:
         head = Gemv(head_case, 1, torch, q)
-        wall, ev_ms = time_launches(torch, head, args.steps, args.warmup, args.warm_seconds)
+        wall, ev_ms = time_launches(torch, head, args.steps, args.warmup, args.warm_seconds,
+                                    scrub)
         per_us = ev_ms * 1e3 / args.steps
         results["q4_k_4096x4096_b1"] = dict(
             weight_bytes=head.wbytes, launches=args.steps,
             wall_gbs=round(args.steps * head.wbytes / wall / 1e9, 1),
             event_us_per_launch=round(per_us, 3),
-            event_gbs=round(head.wbytes / (per_us * 1e-6) / 1e9, 1))
+            event_gbs=round(head.wbytes / (per_us * 1e-6) / 1e9, 1),
+            arith=ARITH["valu_f32"])
         head_wall, head_us = wall, per_us
         del head
 
@@ -357,8 +494,8 @@ def main():
         sweep = [("q8_0_256x1024", 1, False), ("q6_k_151936x2048", 1, False)]
         sweep += [("q5_k_14336x4096", b, False) for b in (1, 4, 8)]
         sweep += [("q4_0_4096x14336", b, False) for b in (1, 4, 8)]
-        # a prefill-sized batch (groups of 8 rows on the matrix cores)
-        sweep += [("q4_k_4096x4096", 32, False)]
+        # prefill-sized batches
+        sweep += [("q4_k_4096x4096", b, False) for b in (16, 32, 64)]
         # the int8-activation variant (batch 1)
         sweep += [("q4_k_4096x4096", 1, True), ("q6_k_151936x2048", 1, True)]
         for name, b, q8 in sweep:
@@ -368,7 +505,7 @@ def main():
             case = synth.GEMV_CASES[name]
             w = Gemv(case, b, torch, q, q8act=q8)
             steps = max(50, min(args.steps, int(4e9 // w.wbytes)))
-            wall, ev_ms = time_launches(torch, w, steps, args.warmup, args.warm_seconds)
+            wall, ev_ms = time_launches(torch, w, steps, args.warmup, args.warm_seconds, scrub)
             per_us = ev_ms * 1e3 / steps
             results[key] = dict(
                 weight_bytes=w.wbytes, launches=steps,
@@ -377,32 +514,61 @@ def main():
                 event_gbs=round(w.wbytes / (per_us * 1e-6) / 1e9, 1),
                 event_frac_hbm=round(w.wbytes / (per_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
                 # multiply-adds of the product, as TFLOP/s (2 flops each)
-                tflops=round(2.0 * case.rows * case.cols * b / (per_us * 1e-6) / 1e12, 2))
+                tflops=round(2.0 * case.rows * case.cols * b / (per_us * 1e-6) / 1e12, 2),
+                arith=gemv_arith(case.fmt, b, q8))
             del w
             torch.cuda.empty_cache()
+        # the streaming floor: a plain read of the headline's and the lm_head's
+        # weight bytes, cold, at a few grid sizes
+        for name in ("q4_k_4096x4096", "q6_k_151936x2048"):
+            case = synth.GEMV_CASES[name]
+            nbytes = case.rows * q.qg_row_bytes(case.fmt, case.cols)
+            key = f"stream_read_{name}_bytes"
+            if only and key not in only:
+                continue
+            best = None
+            for grid in (0, 256, 512, 1024):
+                sw = Stream(nbytes, torch, q, grid)
+                steps = max(50, min(args.steps, int(4e9 // nbytes)))
+                wall, ev_ms = time_launches(torch, sw, steps, args.warmup, args.warm_seconds,
+                                            scrub)
+                per_us = ev_ms * 1e3 / steps
+                if best is None or per_us < best[1]:
+                    best = (grid, per_us, steps)
+                del sw
+                torch.cuda.empty_cache()
+            grid, per_us, steps = best
+            results[key] = dict(
+                bytes=nbytes, launches=steps, best_grid=grid or "auto",
+                event_us_per_launch=round(per_us, 3),
+                event_gbs=round(nbytes / (per_us * 1e-6) / 1e9, 1),
+                event_frac_hbm=round(nbytes / (per_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
+                arith=ARITH["read"])
         if not only or "moe_ffn_qwen3_30b_a3b" in only:
             m = Moe(synth.MOE_CASE, torch, q, args.moe_tokens)
             steps = max(64, min(args.steps, 1000))
-            wall, ev_ms = time_launches(torch, m, steps, args.warmup, args.warm_seconds)
+            wall, ev_ms = time_launches(torch, m, steps, args.warmup, args.warm_seconds, scrub)
             per_us = ev_ms * 1e3 / steps
             results["moe_ffn_qwen3_30b_a3b"] = dict(
                 bytes_per_token=m.bytes_per_token, tokens=steps,
                 wall_tokens_per_s=round(steps / wall, 1),
                 event_us_per_token=round(per_us, 3),
                 tokens_per_s=round(1e6 / per_us, 1),
-                effective_gbs=round(m.bytes_per_token / (per_us * 1e-6) / 1e9, 1))
+                effective_gbs=round(m.bytes_per_token / (per_us * 1e-6) / 1e9, 1),
+                arith=ARITH["moe"])
             del m
         if not only or "moe_ffn_norm_qwen3_30b_a3b" in only:
             m = MoeNorm(synth.MOE_CASE, torch, q, args.moe_tokens)
             steps = max(64, min(args.steps, 1000))
-            wall, ev_ms = time_launches(torch, m, steps, args.warmup, args.warm_seconds)
+            wall, ev_ms = time_launches(torch, m, steps, args.warmup, args.warm_seconds, scrub)
             per_us = ev_ms * 1e3 / steps
             results["moe_ffn_norm_qwen3_30b_a3b"] = dict(
                 bytes_per_token=m.bytes_per_token, tokens=steps,
                 wall_tokens_per_s=round(steps / wall, 1),
                 event_us_per_token=round(per_us, 3),
                 tokens_per_s=round(1e6 / per_us, 1),
-                effective_gbs=round(m.bytes_per_token / (per_us * 1e-6) / 1e9, 1))
+                effective_gbs=round(m.bytes_per_token / (per_us * 1e-6) / 1e9, 1),
+                arith=ARITH["moe"])
             del m
 
         for T in (4, 8):
@@ -411,13 +577,14 @@ def main():
                 continue
             m = MoeTokens(synth.MOE_CASE, torch, q, args.moe_tokens, T)
             steps = max(64, min(args.steps, 500))
-            wall, ev_ms = time_launches(torch, m, steps, args.warmup, args.warm_seconds)
+            wall, ev_ms = time_launches(torch, m, steps, args.warmup, args.warm_seconds, scrub)
             per_us = ev_ms * 1e3 / steps
             results[key] = dict(
                 tokens_per_call=T, calls=steps,
                 wall_tokens_per_s=round(steps * T / wall, 1),
                 event_us_per_call=round(per_us, 3),
-                tokens_per_s=round(T * 1e6 / per_us, 1))
+                tokens_per_s=round(T * 1e6 / per_us, 1),
+                arith=ARITH["moe"])
             del m
 
     line = {
@@ -431,7 +598,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic, seeded (Q4_K fields: d, dmin ~ U[1e-3,1e-2], 6-bit scales and "
-                "nibbles uniform; x ~ N(0,1)); weights cold in HBM",
+                "nibbles uniform; x ~ N(0,1)); weights cold in HBM (rotating copies >= 1 GiB "
+                "and a 1 GiB cache scrub before the timed replay)",
         "config": {"workload": "Q4_K GEMV 4096 x 4096, batch 1", "rows": 4096, "cols": 4096,
                    "batch": 1, "format": "Q4_K", "weight_bytes": head_case.rows * 2304,
                    "cold_copies": True},
@@ -442,11 +610,18 @@ def main():
         line["value"] = r["wall_gbs"]
         line["ms_per_step"] = round(head_wall / args.steps * 1e3, 6)
         achieved = wb / (head_us * 1e-6) / 1e9
-        line["roofline"] = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                            "traffic": measured_traffic(),
-                            "kernel": "qgemv_lds_kernel, Q4_K, 64-column lane tiles, batch 1",
-                            "bytes_per_launch": wb}
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": measured_traffic(),
+                "kernel": "qgemv_lds_kernel, Q4_K, 64-column lane tiles, batch 1",
+                "bytes_per_launch": wb, "event_us_per_launch": round(head_us, 3)}
+        # the same kernel's mean duration in the committed rocprofv3 trace
+        tu = measured_trace_us()
+        roof["trace_us_per_launch"] = tu
+        if tu:
+            roof["trace_achieved"] = round(wb / (tu * 1e-6) / 1e9, 1)
+            roof["trace_frac"] = round(wb / (tu * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        line["roofline"] = roof
     line["workloads"] = results
     if args.copy_calibration:
         n = 256 << 20
@@ -460,6 +635,8 @@ def main():
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
         line["cpu_baseline_all_cores"] = cpu_baseline_all_cores(args.cpu_seconds / 2)
+        if not args.quick:
+            line["cpu_baseline_moe"] = cpu_baseline_moe(args.cpu_seconds / 2)
     print(json.dumps(line), flush=True)
 
 

@@ -40,6 +40,7 @@ SIGNATURES = {
     "moe_ffn_noalloc": ([_P, _P, _P, _P, _INT, _P, _INT, _P, _INT, _P, _I64, _I64, _I64, _I64,
                          _P, _P, _P], _INT),
     "qg_route_topk": ([_P, _I64, _I64, _P, _P, _P], _INT),
+    "qg_stream_read": ([_P, ctypes.c_size_t, _P, _INT, _P], _INT),
     "moe_ffn_tokens_workspace_bytes": ([_I64, _I64, _I64, _I64], ctypes.c_size_t),
     "moe_ffn_tokens": ([_P, _P, _P, _P, _INT, _P, _INT, _P, _INT, _P, _I64, _I64, _I64, _I64,
                         _I64, _P, _P, _P, ctypes.c_size_t, _P], _INT),
@@ -209,3 +210,9 @@ def qgemv_q8act(fmt: int, W, rows: int, cols: int, X, Y, stream=None) -> None:
     """Y = deq(W) * X at batch 1 on int8-quantised activations (see include/qgemv.h)."""
     rc = load_library().qgemv_q8act(fmt, _ptr(W), rows, cols, _ptr(X), _ptr(Y), _stream(stream))
     _check(rc, "qgemv_q8act")
+
+
+def qg_stream_read(buf, nbytes: int, out, grid: int = 0, stream=None) -> None:
+    """Read nbytes of buf once (the streaming floor; see include/qgemv.h)."""
+    rc = load_library().qg_stream_read(_ptr(buf), nbytes, _ptr(out), grid, _stream(stream))
+    _check(rc, "qg_stream_read")

@@ -11,6 +11,44 @@ using namespace qg::host;
 
 namespace {
 
+// Streaming read of `bytes` bytes (a multiple of 16): every thread issues
+// its kLoads 16-byte non-temporal loads of a round before using any, the
+// same cache policy as the GEMVs' weight streams; the XOR of everything
+// read is stored per workgroup so the loads cannot be dropped.
+constexpr int kStreamThreads = 512, kStreamLoads = 4;
+
+__global__ void __launch_bounds__(kStreamThreads) stream_read_kernel(const uint8_t *buf,
+                                                                     uint64_t bytes,
+                                                                     uint32_t *out) {
+    const uint64_t per_round = (uint64_t)gridDim.x * kStreamThreads * kStreamLoads * 16;
+    uint32_t acc = 0;
+    for (uint64_t base = (uint64_t)blockIdx.x * kStreamThreads * kStreamLoads * 16; base < bytes;
+         base += per_round) {
+        const uint64_t rem = bytes - base;
+        const rsrc_t r = make_rsrc(buf + base, rem > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)rem);
+        uint32_t v[kStreamLoads][4];
+#pragma unroll
+        for (int j = 0; j < kStreamLoads; j++) {
+            const auto w = __builtin_amdgcn_raw_buffer_load_b128(
+                r, 16u * (uint32_t)(j * kStreamThreads + (int)threadIdx.x), 0, kStream);
+            v[j][0] = w[0]; v[j][1] = w[1]; v[j][2] = w[2]; v[j][3] = w[3];
+        }
+#pragma unroll
+        for (int j = 0; j < kStreamLoads; j++) acc ^= v[j][0] ^ v[j][1] ^ v[j][2] ^ v[j][3];
+    }
+    // one word per workgroup: the XOR over its threads
+    __shared__ uint32_t red[kStreamThreads / 64];
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t a = 0;
+        for (int w = 0; w < kStreamThreads / 64; w++) a ^= red[w];
+        out[blockIdx.x] = a;
+    }
+}
+
 int try_mx(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
            int batch, int64_t rb, hipStream_t st, bool *done) {
     *done = false;
@@ -317,6 +355,23 @@ int qg_route_topk(const double *logits, int64_t n_experts, int64_t top_k, int32_
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return fail(QG_ELAUNCH, "qg_route_topk: launch failed: %s", hipGetErrorString(e));
+    return ok();
+}
+
+int qg_stream_read(const void *buf, size_t bytes, uint32_t *out, int grid, void *stream) {
+    if (!buf || !out) return fail(QG_EINVAL, "qg_stream_read: buf and out must be non-NULL");
+    if (bytes == 0 || bytes % 16 != 0 || !aligned_to(buf, 16) || !aligned_to(out, 4))
+        return fail(QG_EINVAL, "qg_stream_read: bytes must be a positive multiple of 16 and buf "
+                               "16-byte aligned");
+    const uint64_t per_wg = (uint64_t)kStreamThreads * kStreamLoads * 16;
+    const uint64_t need = (bytes + per_wg - 1) / per_wg;
+    if (grid <= 0) grid = (int)(need < 2048 ? need : 2048);
+    if ((uint64_t)grid > need) grid = (int)need;
+    hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(kStreamThreads), 0,
+                       (hipStream_t)stream, (const uint8_t *)buf, (uint64_t)bytes, out);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(QG_ELAUNCH, "qg_stream_read: launch failed: %s", hipGetErrorString(e));
     return ok();
 }
 

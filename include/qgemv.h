@@ -317,6 +317,25 @@ int moe_ffn_norm(const float *attn_out, const float *hidden_in,
 int qg_route_topk(const double *logits, int64_t n_experts, int64_t top_k,
                   int32_t *sel_experts, float *sel_weights, void *stream);
 
+/*
+ * qg_stream_read: a measurement helper, not a step of the method.  Reads
+ * `bytes` bytes of `buf` once with coalesced 16-byte non-temporal loads
+ * (the cache policy of the GEMVs' weight streams) and stores the XOR of
+ * what each workgroup read to out[workgroup].  Its time is the streaming
+ * floor of a kernel that must read that many bytes, against which the
+ * GEMVs' batch-1 times are read (weight_matrix.rs page, apply_batch notes:
+ * reading the weights is the bottleneck, not the arithmetic).
+ *
+ *   buf    device memory, 16-byte aligned; bytes a positive multiple of 16.
+ *   out    uint32 [grid] (device).
+ *   grid   workgroups of 512 threads (each takes 32 KiB per round, all of a
+ *          round's loads in flight together); <= 0 picks
+ *          min(ceil(bytes / 32 KiB), 2048).  A grid above that count is
+ *          reduced to it.
+ *   stream hipStream_t or NULL.
+ */
+int qg_stream_read(const void *buf, size_t bytes, uint32_t *out, int grid, void *stream);
+
 #ifdef __cplusplus
 }
 #endif
