@@ -74,25 +74,37 @@ int dispatch_gemv_b(int fmt, bool aligned, int cpt, const GemvParams &p, hipStre
     constexpr int U = B == 1 ? QG_U_B1 : QG_U_BN;
     constexpr int K45 = lw_k45(B), Q6 = lw_q6k(B), Q8 = lw_q80(B), Q4 = lw_q40(B);
     constexpr int FM = lw_f32max(B);
-    switch (fmt) {
-    case QG_Q4_K:
-        return aligned ? launch_gemv<FmtQ4K<K45, false>, B, U>(p, st)
-                       : launch_gemv<FmtQ4K<K45, true>, B, U>(p, st);
-    case QG_Q5_K:
-        return aligned ? launch_gemv<FmtQ5K<K45, false>, B, U>(p, st)
-                       : launch_gemv<FmtQ5K<K45, true>, B, U>(p, st);
-    case QG_Q6_K: return launch_gemv<FmtQ6K<Q6>, B, U>(p, st);
-    case QG_Q8_0: return launch_gemv<FmtQ80<Q8>, B, U>(p, st);
-    case QG_Q4_0: return launch_gemv<FmtQ40<Q4>, B, U>(p, st);
-    case QG_F32:
+    // at batch >= 2 the block formats run on the matrix cores (qgemv); this
+    // kernel takes F32 rows there
+    if constexpr (B > 1) {
+        if (fmt != QG_F32) return fail(QG_EUNSUPPORTED, "qgemv: internal: format %d at batch %d",
+                                       fmt, B);
         if (cpt == FM) return launch_gemv<FmtF32<FM>, B, U>(p, st);
         if constexpr (FM > 8)
             if (cpt == FM / 2) return launch_gemv<FmtF32<FM / 2>, B, U>(p, st);
-        if constexpr (FM > 16)
-            if (cpt == FM / 4) return launch_gemv<FmtF32<FM / 4>, B, U>(p, st);
         if (cpt == 8) return launch_gemv<FmtF32<8>, B, U>(p, st);
         return launch_gemv<FmtF32<4>, B, U>(p, st);
-    default: return fail(QG_EUNSUPPORTED, "qgemv: unknown format %d", fmt);
+    } else {
+        switch (fmt) {
+        case QG_Q4_K:
+            return aligned ? launch_gemv<FmtQ4K<K45, false>, B, U>(p, st)
+                           : launch_gemv<FmtQ4K<K45, true>, B, U>(p, st);
+        case QG_Q5_K:
+            return aligned ? launch_gemv<FmtQ5K<K45, false>, B, U>(p, st)
+                           : launch_gemv<FmtQ5K<K45, true>, B, U>(p, st);
+        case QG_Q6_K: return launch_gemv<FmtQ6K<Q6>, B, U>(p, st);
+        case QG_Q8_0: return launch_gemv<FmtQ80<Q8>, B, U>(p, st);
+        case QG_Q4_0: return launch_gemv<FmtQ40<Q4>, B, U>(p, st);
+        case QG_F32:
+            if (cpt == FM) return launch_gemv<FmtF32<FM>, B, U>(p, st);
+            if constexpr (FM > 8)
+                if (cpt == FM / 2) return launch_gemv<FmtF32<FM / 2>, B, U>(p, st);
+            if constexpr (FM > 16)
+                if (cpt == FM / 4) return launch_gemv<FmtF32<FM / 4>, B, U>(p, st);
+            if (cpt == 8) return launch_gemv<FmtF32<8>, B, U>(p, st);
+            return launch_gemv<FmtF32<4>, B, U>(p, st);
+        default: return fail(QG_EUNSUPPORTED, "qgemv: unknown format %d", fmt);
+        }
     }
 }
 

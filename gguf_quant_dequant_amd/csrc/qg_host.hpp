@@ -39,9 +39,6 @@
 #ifndef QG_STAGE
 #define QG_STAGE 1
 #endif
-// Block formats at batch >= QG_MX_MIN_BATCH run on the matrix cores when the
-// activation image and the stage buffers fit in LDS (0 disables).  At batch
-// 1 the VALU kernels are as fast or faster on the measured shapes.
 // Rows per row group and iteration in the MoE gate/up and down kernels.
 #ifndef QG_MOE_GU_U
 #define QG_MOE_GU_U 2
@@ -56,9 +53,6 @@
 #endif
 #ifndef QG_MOE_DN_T128
 #define QG_MOE_DN_T128 0
-#endif
-#ifndef QG_MX_MIN_BATCH
-#define QG_MX_MIN_BATCH 2
 #endif
 
 namespace qg {
@@ -259,6 +253,9 @@ int dispatch_gemv_q8(int fmt, bool aligned, const GemvParams &p, hipStream_t st)
 template <int B>
 int try_mx_b(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
              int batch, int64_t rb, hipStream_t st, bool *done);
+template <int NB>
+int gemm_b(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
+           int batch, int64_t rb, hipStream_t st);
 int dispatch_gateup(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_gateup_tokens(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_down(int fmt, const MoeParams &p, hipStream_t st);

@@ -165,46 +165,6 @@ int try_mx_f(const void *W, int64_t rows, int64_t cols, const float *X, float *Y
         *done = true;
         return launch(pl);
     }
-    // The activation image of the whole row does not fit in LDS: split the
-    // columns into the fewest slices of whole 256-column chunks whose plans
-    // fit (batch >= 3 only, where the VALU kernel is compute-bound), and run
-    // them in order, each adding its sums to Y.  Every weight byte is still
-    // read once.
-    // Each slice is a launch of its own over all row tiles, so slices pay
-    // only when the tiles fill the chip (4096 rows = 128 tiles ran slower
-    // in slices than on the VALU kernel).
-    if (batch < 3 || (rows + mx::kRows - 1) / mx::kRows < device_cus()) return QG_OK;
-    const int64_t nc = (cols + mx::kChunk - 1) / mx::kChunk;
-    constexpr int kMaxSlices = 8;
-    for (int64_t ns = 2; ns <= kMaxSlices && ns <= nc; ns++) {
-        const int64_t per = (nc + ns - 1) / ns * mx::kChunk;  // columns per slice
-        MxPlan sl[kMaxSlices];
-        int n = 0;
-        bool fit = true;
-        for (int64_t c0 = 0; c0 < cols; c0 += per, n++) {
-            const int64_t pc = cols - c0 < per ? cols - c0 : per;
-            const int64_t woff = rb * c0 / cols;  // bytes of c0 columns (whole blocks)
-            const uint8_t *Wp = (const uint8_t *)W + woff;
-            if (!mx_plan<F, B>(Wp, rows, pc, batch, rb, &sl[n])) {
-                fit = false;
-                break;
-            }
-            mx::MxParams &q = sl[n].p;
-            q.w_bytes = (uint64_t)rows * (uint64_t)rb - (uint64_t)woff;
-            q.X = X + c0;
-            q.x_stride = (uint32_t)cols;
-            q.x_bytes = (uint32_t)(4 * (cols * batch - c0));
-            q.Y = Y;
-            q.accumulate = n > 0;
-        }
-        if (!fit) continue;
-        *done = true;
-        for (int i = 0; i < n; i++) {
-            const int rc = launch(sl[i]);
-            if (rc != QG_OK) return rc;
-        }
-        return QG_OK;
-    }
     return QG_OK;
 }
 

@@ -79,14 +79,15 @@ def test_rows_past_the_lane_tile_limit_at_batch_1(fmt):
 
 @pytest.mark.parametrize("fmt,cols", [(Q4_K, 16384), (Q4_0, 14336), (Q6_K, 8192)])
 def test_wide_rows_large_batch(fmt, cols):
-    # batch 8 with more tiles than one row group holds: split into batch chunks
+    # batch 8 on wide rows (many chunks per wave)
     _check(fmt, 23, cols, 8, 3100 + fmt)
 
 
 @pytest.mark.parametrize("fmt", [Q8_0, Q4_0, Q4_K, Q5_K, Q6_K])
 @pytest.mark.parametrize("batch", [9, 16, 33, 64])
 def test_batch_above_eight(fmt, batch):
-    # groups of 8 activation rows, the last one partial
+    # the batched matrix-core kernel: one or two batch blocks of 16 per
+    # launch, launches of up to 32 rows (the last one partial)
     _check(fmt, 45, 512 if fmt in (Q8_0, Q4_0) else 768, batch, 3500 + fmt + batch)
 
 
@@ -103,11 +104,11 @@ def test_batch_32_full_size_headline_shape():
     (Q5_K, 4096, 8, 0), (Q4_0, 14336, 4, 2), (Q8_0, 12320, 8, 2), (Q6_K, 6144, 5, 0),
     (Q4_K, 8448, 3, 2),
 ])
-def test_column_slices_on_the_matrix_cores(fmt, cols, batch, offset):
-    # the activation image of a whole row does not fit in LDS at this batch
-    # and the 8200 rows give 257 row tiles: the columns run as slices of
-    # whole 256-column chunks, each adding to Y (slices start at any weight
-    # alignment; a partial last tile of rows)
+def test_wide_rows_on_the_matrix_cores(fmt, cols, batch, offset):
+    # rows whose activations do not fit the whole-row LDS image of the
+    # batch-2..4 kernel run on the batched kernel; 8200 rows give a partial
+    # last tile, the column ranges of the waves of a tile start at any
+    # weight alignment
     _check(fmt, 8200, cols, batch, 3400 + fmt + batch, offset=offset)
 
 
