@@ -440,93 +440,173 @@ __device__ __forceinline__ bool key_before(uint32_t ah, uint32_t al, int ai, uin
     return (ah > bh) | ((ah == bh) & ((al > bl) | ((al == bl) & (ai < bi))));
 }
 
-// One wave: softmax / top-k / renormalise over E <= 1024 f64 logits.  Lane
-// l holds the keys of experts l, l+64, ...; each of the k rounds takes the
-// best expert not yet taken (lane-local scan, then a butterfly over the
-// wave; the order is total, so every lane ends with the same winner).  All
-// selections are done on 32-bit halves with selects, never with a 64-bit
-// value carried across divergent control flow.  Weights:
-// w_s = exp(l_s - l_0) / sum_{j<k} exp(l_j - l_0), which equals the softmax
-// probabilities renormalised over the chosen set.  Lanes s < k write
-// sel[s], wout[s] (any memory space).
-// Weights of the chosen set, one wave: lane s < k holds chosen expert
-// chosen_e (rank s).  w_s = exp(l_s - l_0) / sum_{j<k} exp(l_j - l_0),
-// the softmax probabilities renormalised over the chosen set.  Lanes s < k
-// write sel[s] and wout[s].
-__device__ __forceinline__ void route_weights(const double *logits, int k, int chosen_e, int *sel,
-                                              float *wout) {
-    const int lane = __lane_id();
-    const int ce = lane < k ? chosen_e : 0;
-    const double ls = logits[ce];
-    const double l0 = __shfl(ls, 0);
-    const double ex_all = exp(ls - l0);
-    const uint64_t exb = __builtin_bit_cast(uint64_t, ex_all);
-    const uint32_t keep = lane < k ? 0xFFFFFFFFu : 0u;
-    const double ex = __builtin_bit_cast(
-        double, ((uint64_t)((uint32_t)(exb >> 32) & keep) << 32) | ((uint32_t)exb & keep));
-    const double den = wave_sum_d(ex);
-    if (lane < k) {
-        sel[lane] = chosen_e;
-        wout[lane] = (float)(ex / den);
-    }
+// The logit of an order key (inverse of order_key; a NaN's key 0 maps back
+// to a NaN, -0.0 to +0.0).
+__device__ __forceinline__ double key_value(uint32_t hi, uint32_t lo) {
+    const uint64_t k = ((uint64_t)hi << 32) | lo;
+    const uint64_t b = (k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k;
+    return __builtin_bit_cast(double, b);
 }
 
+template <int CTRL>
+__device__ __forceinline__ double dpp_d(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = dpp_u<CTRL>((uint32_t)b), hi = dpp_u<CTRL>((uint32_t)(b >> 32));
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// A double of lane `src` (uniform), read half by half (readlane returns a
+// signed int: each half is widened as unsigned).
+__device__ __forceinline__ double readlane_d(double v, int src) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, src);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), src);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// Sum over each aligned group of 32 lanes (fixed tree); every lane of a
+// group receives its group's sum.
+__device__ __forceinline__ double group_sum32_d(double v) {
+    v += dpp_d<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp_d<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp_d<0x141>(v);  // row_half_mirror
+    v += dpp_d<0x140>(v);  // row_mirror
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = swz16_u((uint32_t)b), hi = swz16_u((uint32_t)(b >> 32));
+    return v + __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+
+// One wave: softmax / top-k / renormalise over E <= 1024 f64 logits (the
+// module doc's routing on the aprender-serve page).  Lane l holds the
+// order keys of experts l, l + 64, ... (PER slots).  Selection:
+//   1. the k-th largest high key half T, found bit by bit from the top:
+//      T | bit is kept when at least k keys have a high half >= it (a
+//      ballot and a population count per slot and bit);
+//   2. keys above T are chosen; among the keys equal to T the same descent
+//      on the low halves picks the rest, and among fully equal keys the
+//      lowest expert indices (expert l + 64 i orders by slot, then lane);
+//   3. each chosen key's rank is the number of chosen keys before it
+//      (larger key, or equal key and lower index), and lane s takes the
+//      expert of rank s.
+// Every step is a wave-uniform scalar loop or plain compares; no 64-bit
+// value crosses divergent control flow.  Weights: each chosen key forms
+// exp(l - l_0) in f64 from its own key (l_0 the logit of rank 0), the sum
+// over the chosen keys is a fixed tree in f64, and w = exp(l - l_0) / sum,
+// the softmax probabilities renormalised over the chosen set.  The lane
+// holding the key of rank s writes sel[s] and wout[s] (any memory space).
 template <int PER>
 __device__ void route_topk_per(const double *__restrict__ logits, int E, int k, int *sel,
                                float *wout) {
-    constexpr int NONE = 0x7FFFFFFF;
     const int lane = __lane_id();
     uint32_t kh[PER], kl[PER];
+    bool valid[PER];
 #pragma unroll
     for (int i = 0; i < PER; i++) {
         const int e = lane + 64 * i;
-        const double v = logits[e < E ? e : 0];
-        order_key(v, &kh[i], &kl[i]);
+        valid[i] = e < E;
+        order_key(logits[valid[i] ? e : 0], &kh[i], &kl[i]);
     }
-    uint32_t avail = 0;
+    // 1. k-th largest high half
+    uint32_t T = 0;
+    for (int b = 31; b >= 0; b--) {
+        const uint32_t c = T | (1u << b);
+        int n = 0;
 #pragma unroll
-    for (int i = 0; i < PER; i++) avail |= (lane + 64 * i < E) ? (1u << i) : 0u;
-
-    int chosen_e = 0;
-    for (int s = 0; s < k; s++) {
-        uint32_t bh = 0, bl = 0;
-        int bi = NONE;
+        for (int i = 0; i < PER; i++) n += __popcll(__ballot(valid[i] && kh[i] >= c));
+        T = n >= k ? c : T;
+    }
+    // 2. the chosen set, as one ballot mask per slot
+    uint64_t msel[PER];
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const uint64_t gt = __ballot(valid[i] && kh[i] > T);
+        const uint64_t eq = __ballot(valid[i] && kh[i] == T);
+        ngt += __popcll(gt);
+        neq += __popcll(eq);
+        msel[i] = gt | eq;
+    }
+    const int need = k - ngt;
+    if (neq > need) {
+        // several keys share the high half T: descend on the low halves
+        uint32_t TL = 0;
+        for (int b = 31; b >= 0; b--) {
+            const uint32_t c = TL | (1u << b);
+            int n = 0;
+#pragma unroll
+            for (int i = 0; i < PER; i++)
+                n += __popcll(__ballot(valid[i] && kh[i] == T && kl[i] >= c));
+            TL = n >= need ? c : TL;
+        }
+        uint64_t g2[PER], e2[PER];
+        int n2 = 0;
 #pragma unroll
         for (int i = 0; i < PER; i++) {
-            const int e = lane + 64 * i;
-            const bool take = ((avail >> i) & 1u) && key_before(kh[i], kl[i], e, bh, bl, bi);
-            bh = take ? kh[i] : bh;
-            bl = take ? kl[i] : bl;
-            bi = take ? e : bi;
+            g2[i] = __ballot(valid[i] && kh[i] == T && kl[i] > TL);
+            e2[i] = __ballot(valid[i] && kh[i] == T && kl[i] == TL);
+            n2 += __popcll(g2[i]);
         }
-        // best over the wave: DPP within rows of 16, a swizzle across the
-        // two rows of each half, then the two halves through readlane
-        auto take_best = [&](uint32_t oh, uint32_t ol, int oi) {
-            const bool take = key_before(oh, ol, oi, bh, bl, bi);
-            bh = take ? oh : bh;
-            bl = take ? ol : bl;
-            bi = take ? oi : bi;
-        };
-        take_best(dpp_u<0xB1>(bh), dpp_u<0xB1>(bl), (int)dpp_u<0xB1>((uint32_t)bi));
-        take_best(dpp_u<0x4E>(bh), dpp_u<0x4E>(bl), (int)dpp_u<0x4E>((uint32_t)bi));
-        take_best(dpp_u<0x141>(bh), dpp_u<0x141>(bl), (int)dpp_u<0x141>((uint32_t)bi));
-        take_best(dpp_u<0x140>(bh), dpp_u<0x140>(bl), (int)dpp_u<0x140>((uint32_t)bi));
-        take_best(swz16_u(bh), swz16_u(bl), (int)swz16_u((uint32_t)bi));
-        {
-            const uint32_t h0 = __builtin_amdgcn_readlane(bh, 0), l0 = __builtin_amdgcn_readlane(bl, 0);
-            const int i0 = __builtin_amdgcn_readlane(bi, 0);
-            const uint32_t h1 = __builtin_amdgcn_readlane(bh, 32), l1 = __builtin_amdgcn_readlane(bl, 32);
-            const int i1 = __builtin_amdgcn_readlane(bi, 32);
-            const bool t = key_before(h1, l1, i1, h0, l0, i0);
-            bh = t ? h1 : h0;
-            bl = t ? l1 : l0;
-            bi = t ? i1 : i0;
+        int rest = need - n2;  // fully equal keys still to take, lowest index first
+#pragma unroll
+        for (int i = 0; i < PER; i++) {
+            uint64_t m = e2[i], keep = 0;
+            while (rest > 0 && m) {
+                const uint64_t low = m & (~m + 1);
+                keep |= low;
+                m &= m - 1;
+                rest--;
+            }
+            msel[i] = __ballot(valid[i] && kh[i] > T) | g2[i] | keep;
         }
-        const uint32_t mine = (lane == (bi & 63)) ? (1u << ((bi >> 6) & 31)) : 0u;
-        avail &= ~mine;
-        chosen_e = (lane == s) ? bi : chosen_e;
     }
-    route_weights(logits, k, chosen_e, sel, wout);
+    // 3. ranks within the chosen set
+    int rank[PER];
+#pragma unroll
+    for (int i = 0; i < PER; i++) rank[i] = 0;
+#pragma unroll
+    for (int i2 = 0; i2 < PER; i2++) {
+        uint64_t m = msel[i2];
+        while (m) {
+            const int j = __builtin_ctzll(m);
+            m &= m - 1;
+            const uint32_t bh = (uint32_t)__builtin_amdgcn_readlane((int)kh[i2], j);
+            const uint32_t bl = (uint32_t)__builtin_amdgcn_readlane((int)kl[i2], j);
+            const int be = j + 64 * i2;
+#pragma unroll
+            for (int i = 0; i < PER; i++)
+                rank[i] += key_before(bh, bl, be, kh[i], kl[i], lane + 64 * i) ? 1 : 0;
+        }
+    }
+    // weights: every chosen key forms exp(l - l_0) from its own key, l_0
+    // the logit of rank 0; the sum over the chosen keys is a fixed tree in
+    // f64 (per lane over its slots, then the wave)
+    uint32_t h0 = 0, lo0 = 0;
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const uint64_t m = __ballot(((msel[i] >> lane) & 1ull) && rank[i] == 0);
+        if (m) {
+            const int j = __builtin_ctzll(m);
+            h0 = (uint32_t)__builtin_amdgcn_readlane((int)kh[i], j);
+            lo0 = (uint32_t)__builtin_amdgcn_readlane((int)kl[i], j);
+        }
+    }
+    const double l0 = key_value(h0, lo0);
+    double ex[PER], part = 0.0;
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        const bool chosen = (msel[i] >> lane) & 1ull;
+        ex[i] = chosen ? exp(key_value(kh[i], kl[i]) - l0) : 0.0;
+        part += ex[i];
+    }
+    const double half = group_sum32_d(part);
+    const double den = readlane_d(half, 0) + readlane_d(half, 32);
+#pragma unroll
+    for (int i = 0; i < PER; i++) {
+        if ((msel[i] >> lane) & 1ull) {
+            sel[rank[i]] = lane + 64 * i;
+            wout[rank[i]] = (float)(ex[i] / den);
+        }
+    }
 }
 
 // Each lane holds ceil(E/64) keys, rounded up to a power of two, so the k

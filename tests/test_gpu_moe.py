@@ -215,3 +215,17 @@ def test_route_nan_logits_rank_last():
     lg = np.array([np.nan, 3.0, np.nan, -1.0, 0.0])
     sel, _ = _gpu_route(lg, 4)
     assert list(sel) == list(oracle.route(lg, 4)[0]) == [1, 4, 3, 0]
+
+
+@pytest.mark.parametrize("E,k", [(6, 4), (128, 8), (300, 9), (1024, 32)])
+def test_route_all_negative_logits(E, k):
+    # every chosen logit negative (order keys with the sign flipped) and
+    # low key halves with the top bit set: the weights are formed from the
+    # chosen keys themselves
+    g = np.random.default_rng(80 + E)
+    lg = -np.abs(g.standard_normal(E)) - 0.5
+    sel, w = _gpu_route(lg, k)
+    rs, rw = oracle.route(lg, k)
+    assert np.array_equal(sel, rs)
+    assert np.allclose(w, rw, rtol=1e-6, atol=0)
+    assert abs(float(np.sum(w.astype(np.float64))) - 1.0) < 1e-6
