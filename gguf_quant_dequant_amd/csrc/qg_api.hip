@@ -155,8 +155,9 @@ int moe_ffn_impl(const char *who, const float *x, const float *residual, float *
     const int64_t rbg = qg_row_bytes(gate_fmt, hidden), rbd = qg_row_bytes(down_fmt, expert_dim);
     const uint64_t gate_bytes = (uint64_t)n_experts * expert_dim * rbg;
     const uint64_t down_bytes = (uint64_t)n_experts * hidden * rbd;
-    if (gate_bytes > 0xFFFFFFFFull || down_bytes > 0xFFFFFFFFull)
-        return fail(QG_EUNSUPPORTED, "%s: each expert stack must be under 4 GiB", who);
+    // stacks are addressed with 32-bit offsets below kOorRow (4 GiB - 64 KiB)
+    if (gate_bytes > kOorRow - 16u || down_bytes > kOorRow - 16u)
+        return fail(QG_EUNSUPPORTED, "%s: each expert stack must be under 4 GiB - 64 KiB", who);
     if (hidden % moe_cpt(gate_fmt) != 0 || expert_dim % moe_cpt(down_fmt) != 0)
         return fail(QG_EUNSUPPORTED, "%s: sizes do not tile", who);
     if (hidden / moe_cpt(gate_fmt) > 512 || top_k * (expert_dim / moe_cpt(down_fmt)) > 512)

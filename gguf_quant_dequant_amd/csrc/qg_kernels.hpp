@@ -53,13 +53,20 @@ struct GemvParams {
 // that only partly overlaps the array is read whole (its other bytes lie in
 // the same page), while the hardware returns zero for a dword that overlaps
 // the record range only in part.
+// Row offset of a load that is not wanted: every resource built by
+// rows_rsrc ends at or below it, so the load reads zeros and touches no
+// memory.  Loads under a branch would wait for each other (a realigning
+// load uses its data at once and the compiler keeps it inside the branch),
+// so unwanted rows are loaded from here instead of being skipped.
+constexpr uint32_t kOorRow = 0xFFFF0000u;
+
 __device__ __forceinline__ rsrc_t rows_rsrc(const uint8_t *W, uint64_t w_bytes, uint64_t start,
                                             uint32_t *delta) {
     const uint8_t *base = W + start;
     const uint8_t *abase = (const uint8_t *)((uintptr_t)base & ~(uintptr_t)3);
     *delta = (uint32_t)(base - abase);
     const uint64_t rem = (w_bytes - start + *delta + 3) & ~(uint64_t)3;
-    return make_rsrc(abase, rem > 0xFFFFFFFCull ? 0xFFFFFFFCu : (uint32_t)rem);
+    return make_rsrc(abase, rem > kOorRow ? kOorRow : (uint32_t)rem);
 }
 
 template <class F, int B, int U>
@@ -72,8 +79,9 @@ __device__ __forceinline__ void gemv_issue(const GemvParams &p, int64_t it, int 
     const int64_t rg = r0 + (int64_t)grp * U;
 #pragma unroll
     for (int u = 0; u < U; u++)
-        if (active && rg + u < p.rows)
-            F::load(BufReader{rs}, delta + (uint32_t)(grp * U + u) * p.row_bytes, L, raw[u]);
+        F::load(BufReader{rs},
+                active && rg + u < p.rows ? delta + (uint32_t)(grp * U + u) * p.row_bytes : kOorRow,
+                L, raw[u]);
 }
 
 // Dequantise-and-dot of one block of rows already loaded into raw, then the
@@ -476,27 +484,43 @@ __device__ __forceinline__ double group_sum32_d(double v) {
     return v + __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
 }
 
+// LDS one routing wave gathers its chosen keys in: per chosen key its high
+// half, low half and expert index.
+struct RouteLds {
+    uint32_t e[kMaxTopK][4];
+};
+
+__device__ __forceinline__ uint64_t ballot64(bool p) { return __builtin_amdgcn_ballot_w64(p); }
+
+// Number of set bits of m in the lanes below this one.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
 // One wave: softmax / top-k / renormalise over E <= 1024 f64 logits (the
 // module doc's routing on the aprender-serve page).  Lane l holds the
-// order keys of experts l, l + 64, ... (PER slots).  Selection:
-//   1. the k-th largest high key half T, found bit by bit from the top:
-//      T | bit is kept when at least k keys have a high half >= it (a
-//      ballot and a population count per slot and bit);
+// order keys of experts l, l + 64, ... (PER slots); a slot past E holds
+// key 0, as a NaN does.  Selection:
+//   1. the k-th largest high key half T, two bits at a time from the top:
+//      of T | 3 << b, T | 2 << b and T | 1 << b the largest that at least
+//      k high halves reach is kept (ballots and population counts; every
+//      threshold tried is >= 1, so the zero keys of slots past E never
+//      count);
 //   2. keys above T are chosen; among the keys equal to T the same descent
 //      on the low halves picks the rest, and among fully equal keys the
 //      lowest expert indices (expert l + 64 i orders by slot, then lane);
-//   3. each chosen key's rank is the number of chosen keys before it
-//      (larger key, or equal key and lower index), and lane s takes the
-//      expert of rank s.
-// Every step is a wave-uniform scalar loop or plain compares; no 64-bit
-// value crosses divergent control flow.  Weights: each chosen key forms
-// exp(l - l_0) in f64 from its own key (l_0 the logit of rank 0), the sum
-// over the chosen keys is a fixed tree in f64, and w = exp(l - l_0) / sum,
-// the softmax probabilities renormalised over the chosen set.  The lane
-// holding the key of rank s writes sel[s] and wout[s] (any memory space).
+//   3. the chosen keys are gathered in expert order into LDS; lane s < k
+//      takes the s-th and counts the gathered keys that rank before it
+//      (larger key, or equal key and lower index): that count is its rank.
+// Weights: lane s forms exp(l_s - l_0) in f64 (l_0 the logit of rank 0),
+// the sum over the k chosen keys is a fixed tree in f64 over lanes
+// 0 .. k-1, and w = exp(l_s - l_0) / sum, the softmax probabilities
+// renormalised over the chosen set.  The lane of rank r writes sel[r] and
+// wout[r] (any memory space).
 template <int PER>
-__device__ void route_topk_per(const double *__restrict__ logits, int E, int k, int *sel,
-                               float *wout) {
+__device__ __forceinline__ void route_topk_per(const double *__restrict__ logits, int E, int k,
+                                               int *sel, float *wout, RouteLds *lds) {
     const int lane = __lane_id();
     uint32_t kh[PER], kl[PER];
     bool valid[PER];
@@ -505,45 +529,64 @@ __device__ void route_topk_per(const double *__restrict__ logits, int E, int k, 
         const int e = lane + 64 * i;
         valid[i] = e < E;
         order_key(logits[valid[i] ? e : 0], &kh[i], &kl[i]);
+        kh[i] = valid[i] ? kh[i] : 0u;
+        kl[i] = valid[i] ? kl[i] : 0u;
     }
-    // 1. k-th largest high half
+    // 1. k-th largest high half.  T only grows and at least k high halves
+    // reach it; once exactly k do, those k are the chosen set and the
+    // remaining bits cannot change it, so the descent stops there.
     uint32_t T = 0;
-    for (int b = 31; b >= 0; b--) {
-        const uint32_t c = T | (1u << b);
-        int n = 0;
+#pragma unroll 1
+    for (int b = 30; b >= 0; b -= 2) {
+        const uint32_t c1 = T | (1u << b), c2 = T | (2u << b), c3 = T | (3u << b);
+        int n1 = 0, n2 = 0, n3 = 0;
 #pragma unroll
-        for (int i = 0; i < PER; i++) n += __popcll(__ballot(valid[i] && kh[i] >= c));
-        T = n >= k ? c : T;
+        for (int i = 0; i < PER; i++) {
+            n1 += __popcll(ballot64(kh[i] >= c1));
+            n2 += __popcll(ballot64(kh[i] >= c2));
+            n3 += __popcll(ballot64(kh[i] >= c3));
+        }
+        T = n3 >= k ? c3 : (n2 >= k ? c2 : (n1 >= k ? c1 : T));
+        if ((n3 == k) | ((n3 < k) & (n2 == k)) | ((n2 < k) & (n1 == k))) break;
     }
     // 2. the chosen set, as one ballot mask per slot
     uint64_t msel[PER];
     int ngt = 0, neq = 0;
 #pragma unroll
     for (int i = 0; i < PER; i++) {
-        const uint64_t gt = __ballot(valid[i] && kh[i] > T);
-        const uint64_t eq = __ballot(valid[i] && kh[i] == T);
+        const uint64_t gt = ballot64(kh[i] > T);
+        const uint64_t eq = ballot64(valid[i] && kh[i] == T);
         ngt += __popcll(gt);
         neq += __popcll(eq);
         msel[i] = gt | eq;
     }
     const int need = k - ngt;
     if (neq > need) {
-        // several keys share the high half T: descend on the low halves
-        uint32_t TL = 0;
-        for (int b = 31; b >= 0; b--) {
-            const uint32_t c = TL | (1u << b);
-            int n = 0;
+        // several keys share the high half T: descend on the low halves of
+        // those keys (the others take low half 0, below every threshold)
+        uint32_t lt[PER];
 #pragma unroll
-            for (int i = 0; i < PER; i++)
-                n += __popcll(__ballot(valid[i] && kh[i] == T && kl[i] >= c));
-            TL = n >= need ? c : TL;
+        for (int i = 0; i < PER; i++) lt[i] = (valid[i] && kh[i] == T) ? kl[i] : 0u;
+        uint32_t TL = 0;
+#pragma unroll 1
+        for (int b = 30; b >= 0; b -= 2) {
+            const uint32_t c1 = TL | (1u << b), c2 = TL | (2u << b), c3 = TL | (3u << b);
+            int n1 = 0, n2 = 0, n3 = 0;
+#pragma unroll
+            for (int i = 0; i < PER; i++) {
+                n1 += __popcll(ballot64(lt[i] >= c1));
+                n2 += __popcll(ballot64(lt[i] >= c2));
+                n3 += __popcll(ballot64(lt[i] >= c3));
+            }
+            TL = n3 >= need ? c3 : (n2 >= need ? c2 : (n1 >= need ? c1 : TL));
         }
         uint64_t g2[PER], e2[PER];
         int n2 = 0;
 #pragma unroll
         for (int i = 0; i < PER; i++) {
-            g2[i] = __ballot(valid[i] && kh[i] == T && kl[i] > TL);
-            e2[i] = __ballot(valid[i] && kh[i] == T && kl[i] == TL);
+            const bool eqT = valid[i] && kh[i] == T;
+            g2[i] = ballot64(eqT && kl[i] > TL);
+            e2[i] = ballot64(eqT && kl[i] == TL);
             n2 += __popcll(g2[i]);
         }
         int rest = need - n2;  // fully equal keys still to take, lowest index first
@@ -556,74 +599,71 @@ __device__ void route_topk_per(const double *__restrict__ logits, int E, int k, 
                 m &= m - 1;
                 rest--;
             }
-            msel[i] = __ballot(valid[i] && kh[i] > T) | g2[i] | keep;
+            msel[i] = ballot64(kh[i] > T) | g2[i] | keep;
         }
     }
-    // 3. ranks within the chosen set
-    int rank[PER];
-#pragma unroll
-    for (int i = 0; i < PER; i++) rank[i] = 0;
-#pragma unroll
-    for (int i2 = 0; i2 < PER; i2++) {
-        uint64_t m = msel[i2];
-        while (m) {
-            const int j = __builtin_ctzll(m);
-            m &= m - 1;
-            const uint32_t bh = (uint32_t)__builtin_amdgcn_readlane((int)kh[i2], j);
-            const uint32_t bl = (uint32_t)__builtin_amdgcn_readlane((int)kl[i2], j);
-            const int be = j + 64 * i2;
-#pragma unroll
-            for (int i = 0; i < PER; i++)
-                rank[i] += key_before(bh, bl, be, kh[i], kl[i], lane + 64 * i) ? 1 : 0;
-        }
-    }
-    // weights: every chosen key forms exp(l - l_0) from its own key, l_0
-    // the logit of rank 0; the sum over the chosen keys is a fixed tree in
-    // f64 (per lane over its slots, then the wave)
-    uint32_t h0 = 0, lo0 = 0;
+    // 3. gather the chosen keys in expert order, then rank them
+    int base = 0;
 #pragma unroll
     for (int i = 0; i < PER; i++) {
-        const uint64_t m = __ballot(((msel[i] >> lane) & 1ull) && rank[i] == 0);
-        if (m) {
-            const int j = __builtin_ctzll(m);
-            h0 = (uint32_t)__builtin_amdgcn_readlane((int)kh[i], j);
-            lo0 = (uint32_t)__builtin_amdgcn_readlane((int)kl[i], j);
+        const int pos = base + lanes_below(msel[i]);
+        if (((msel[i] >> lane) & 1ull) && pos < kMaxTopK) {
+            lds->e[pos][0] = kh[i];
+            lds->e[pos][1] = kl[i];
+            lds->e[pos][2] = (uint32_t)(lane + 64 * i);
         }
+        base += __popcll(msel[i]);
     }
-    const double l0 = key_value(h0, lo0);
-    double ex[PER], part = 0.0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const bool mine = lane < k;
+    const int s = mine ? lane : 0;
+    const uint32_t oh = lds->e[s][0], ol = lds->e[s][1];
+    const int oi = (int)lds->e[s][2];
+    // eight gathered keys per round, all read before any is compared
+    // (entries past k are read but not counted)
+    int rank = 0;
+#pragma unroll 1
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        uint32_t v[8][3];
 #pragma unroll
-    for (int i = 0; i < PER; i++) {
-        const bool chosen = (msel[i] >> lane) & 1ull;
-        ex[i] = chosen ? exp(key_value(kh[i], kl[i]) - l0) : 0.0;
-        part += ex[i];
+        for (int u = 0; u < 8; u++)
+#pragma unroll
+            for (int q = 0; q < 3; q++) v[u][q] = lds->e[j0 + u][q];
+#pragma unroll
+        for (int u = 0; u < 8; u++)
+            rank += (j0 + u < k && key_before(v[u][0], v[u][1], (int)v[u][2], oh, ol, oi)) ? 1 : 0;
     }
-    const double half = group_sum32_d(part);
-    const double den = readlane_d(half, 0) + readlane_d(half, 32);
-#pragma unroll
-    for (int i = 0; i < PER; i++) {
-        if ((msel[i] >> lane) & 1ull) {
-            sel[rank[i]] = lane + 64 * i;
-            wout[rank[i]] = (float)(ex[i] / den);
-        }
+    // weights
+    const uint64_t m0 = ballot64(mine && rank == 0);
+    const int j0 = m0 ? (int)__builtin_ctzll(m0) : 0;
+    const uint32_t h0 = (uint32_t)__builtin_amdgcn_readlane((int)oh, j0);
+    const uint32_t lo0 = (uint32_t)__builtin_amdgcn_readlane((int)ol, j0);
+    const double ex = mine ? exp(key_value(oh, ol) - key_value(h0, lo0)) : 0.0;
+    const double den = readlane_d(group_sum32_d(ex), 0);  // k <= 32: lanes 0 .. 31
+    if (mine) {
+        sel[rank] = oi;
+        wout[rank] = (float)(ex / den);
     }
 }
 
 // Each lane holds ceil(E/64) keys, rounded up to a power of two, so the k
 // selection rounds scan only as many slots as the expert count needs.
-__device__ void route_topk_wave(const double *__restrict__ logits, int E, int k, int *sel,
-                                float *wout) {
+// `lds` is this wave's own gathering area.
+__device__ __forceinline__ void route_topk_wave(const double *__restrict__ logits, int E, int k,
+                                                int *sel, float *wout, RouteLds *lds) {
     static_assert(kMaxExperts == 64 * 16, "slot dispatch covers up to 16 keys per lane");
     if (E <= 64)
-        route_topk_per<1>(logits, E, k, sel, wout);
+        route_topk_per<1>(logits, E, k, sel, wout, lds);
     else if (E <= 128)
-        route_topk_per<2>(logits, E, k, sel, wout);
+        route_topk_per<2>(logits, E, k, sel, wout, lds);
     else if (E <= 256)
-        route_topk_per<4>(logits, E, k, sel, wout);
+        route_topk_per<4>(logits, E, k, sel, wout, lds);
     else if (E <= 512)
-        route_topk_per<8>(logits, E, k, sel, wout);
+        route_topk_per<8>(logits, E, k, sel, wout, lds);
     else
-        route_topk_per<16>(logits, E, k, sel, wout);
+        route_topk_per<16>(logits, E, k, sel, wout, lds);
 }
 
 
@@ -657,12 +697,6 @@ struct MoeParams {
     int32_t T;
 };
 
-// The residual stream of row r: residual[r], or the f32 sum residual[r] +
-// residual2[r] when the residual add of the norm step is fused here.
-__device__ __forceinline__ float moe_residual(const MoeParams &p, int64_t r) {
-    return p.residual2 ? p.residual[r] + p.residual2[r] : p.residual[r];
-}
-
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g)); }
 
 // ------------------------------------------------------------------ MoE K2
@@ -670,6 +704,7 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + expf(-g));
 template <class F, int U>
 __global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
     __shared__ int s_sel[kMaxTopK];
+    __shared__ RouteLds s_rt[1];
     __shared__ float s_w[kMaxTopK];
     __shared__ float red[8][2 * U];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -690,7 +725,7 @@ __global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
     const rsrc_t rx = make_rsrc(p.x, 4u * H);
     uint32_t xr[kStageChunks][4];
     xs_fetch(rx, 0u, (H < xcap ? H : xcap) / 4u, tid, nthr, xr);
-    if (wave == 0) route_topk_wave(p.logits, p.E, p.K, s_sel, s_w);
+    if (wave == 0) route_topk_wave(p.logits, p.E, p.K, s_sel, s_w, &s_rt[0]);
     typename F::template XTile<1> xt;
     {
         const uint32_t xbase[1] = {0u};
@@ -716,12 +751,11 @@ __global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const int64_t t = t0 + u;
-            if (active && t < tasks) {
-                const int s = (int)(t / p.F), j = (int)(t % p.F);
-                const uint32_t off = ((uint32_t)s_sel[s] * (uint32_t)p.F + (uint32_t)j) * p.rb_gate;
-                F::load(BufReader{rg}, dg + off, L, rawg[u]);
-                F::load(BufReader{ru}, du + off, L, rawu[u]);
-            }
+            const bool want = active && t < tasks;
+            const int s = want ? (int)(t / p.F) : 0, j = want ? (int)(t % p.F) : 0;
+            const uint32_t off = ((uint32_t)s_sel[s] * (uint32_t)p.F + (uint32_t)j) * p.rb_gate;
+            F::load(BufReader{rg}, want ? dg + off : kOorRow, L, rawg[u]);
+            F::load(BufReader{ru}, want ? du + off : kOorRow, L, rawu[u]);
         }
         float ag[U][1], au[U][1];
 #pragma unroll
@@ -825,6 +859,7 @@ __device__ __forceinline__ int distinct_experts(const int *s_sel, int nroutes, i
 template <class F, int B, int U>
 __global__ void __launch_bounds__(512) moe_gateup_tokens_kernel(MoeParams p) {
     __shared__ int s_sel[kMaxRoutes];
+    __shared__ RouteLds s_rt[8];  // one per wave (blockDim <= 512)
     __shared__ float s_w[kMaxRoutes];
     __shared__ int s_uexp[kMaxRoutes];
     __shared__ int s_uslot[kMaxRoutes][kMaxTokens];
@@ -853,7 +888,8 @@ __global__ void __launch_bounds__(512) moe_gateup_tokens_kernel(MoeParams p) {
     uint32_t xr[kStageChunks][4];
     xs_fetch(rx, 0u, (xtot < xcap ? xtot : xcap) / 4u, tid, nthr, xr);
     for (int t = wave; t < T; t += (int)(blockDim.x >> 6))
-        route_topk_wave(p.logits + (int64_t)t * p.E, p.E, K, s_sel + t * K, s_w + t * K);
+        route_topk_wave(p.logits + (int64_t)t * p.E, p.E, K, s_sel + t * K, s_w + t * K,
+                        &s_rt[wave]);
     typename F::template XTile<B> xt;
     {
         uint32_t xbase[B];
@@ -886,13 +922,11 @@ __global__ void __launch_bounds__(512) moe_gateup_tokens_kernel(MoeParams p) {
 #pragma unroll
         for (int u = 0; u < U; u++) {
             const int64_t t = t0 + u;
-            if (active && t < tasks) {
-                const int ue = (int)(t / p.F), j = (int)(t % p.F);
-                const uint32_t off =
-                    ((uint32_t)s_uexp[ue] * (uint32_t)p.F + (uint32_t)j) * p.rb_gate;
-                F::load(BufReader{rg}, dg + off, L, rawg[u]);
-                F::load(BufReader{ru}, du + off, L, rawu[u]);
-            }
+            const bool want = active && t < tasks;
+            const int ue = want ? (int)(t / p.F) : 0, j = want ? (int)(t % p.F) : 0;
+            const uint32_t off = ((uint32_t)s_uexp[ue] * (uint32_t)p.F + (uint32_t)j) * p.rb_gate;
+            F::load(BufReader{rg}, want ? dg + off : kOorRow, L, rawg[u]);
+            F::load(BufReader{ru}, want ? du + off : kOorRow, L, rawu[u]);
         }
         float v[2 * U * B];
 #pragma unroll
@@ -983,6 +1017,46 @@ __global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
     xs_fetch(ra, 0u, (xtot < xcap ? xtot : xcap) / 4u, tid, nthr, xr);
     const uint32_t expert_off =
         active ? (uint32_t)p.ws_sel[slot] * (uint32_t)p.H * p.rb_down : 0u;
+    uint32_t dd;
+    const rsrc_t rd = rows_rsrc(p.down, p.down_bytes, 0, &dd);
+    const int64_t rpi = (int64_t)p.dn_G * U;
+    // the first rows' weight loads go out as soon as the routes are in,
+    // ahead of the activation staging; each later round's loads are issued
+    // at the end of the round before
+    typename F::Raw raw[U];
+    auto issue = [&](int64_t it) {
+        const int64_t r0 = it * rpi + (int64_t)grp * U;
+#pragma unroll
+        for (int u = 0; u < U; u++)
+            F::load(BufReader{rd},
+                    active && r0 + u < p.H ? dd + expert_off + (uint32_t)(r0 + u) * p.rb_down
+                                           : kOorRow,
+                    L, raw[u]);
+    };
+    // the residual rows each writing lane adds, loaded with the weights:
+    // U rows r0 + u for a row group's lane 0 (one-wave rows), row r0 + lane
+    // for lanes below U of a group's first wave (rows over several waves);
+    // rows past H read as zero.  With the norm step's residual add fused
+    // here the residual is residual + residual2, added in f32.
+    const uint32_t hb = 4u * (uint32_t)p.H;
+    const rsrc_t rres = make_rsrc(p.residual, hb);
+    const rsrc_t rres2 = make_rsrc(p.residual2 ? p.residual2 : p.residual, hb);
+    auto fetch_res = [&](int64_t it, float (&rv)[U]) {
+        const int64_t r0 = it * rpi + (int64_t)grp * U;
+#pragma unroll
+        for (int u = 0; u < U; u++) {
+            const int64_t r = p.dn_S == 1 ? r0 + u : r0 + lane;
+            const uint32_t off = r < p.H ? 4u * (uint32_t)r : 0xFFFFFFF0u;
+            const float a = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rres, off, 0, 0));
+            const float b = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rres2, off, 0, 0));
+            rv[u] = p.residual2 ? a + b : a;
+        }
+    };
+    float resv[U];
+    if ((int64_t)blockIdx.x * rpi < p.H) {
+        issue(blockIdx.x);
+        fetch_res(blockIdx.x, resv);
+    }
     typename F::template XTile<1> xt;
     {
         const uint32_t xbase[1] = {(uint32_t)slot * (uint32_t)p.F};
@@ -990,21 +1064,18 @@ __global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
         xs_stage<F, 1>(xst, ra, xtot, xbase, L, active, tid, nthr, xr, x);
         F::template prep<1>(x, xt);
     }
-    uint32_t dd;
-    const rsrc_t rd = rows_rsrc(p.down, p.down_bytes, 0, &dd);
-    const int64_t rpi = (int64_t)p.dn_G * U;
     for (int64_t it = blockIdx.x; it * rpi < p.H; it += gridDim.x) {
         const int64_t r0 = it * rpi + (int64_t)grp * U;
-        typename F::Raw raw[U];
-#pragma unroll
-        for (int u = 0; u < U; u++)
-            if (active && r0 + u < p.H)
-                F::load(BufReader{rd}, dd + expert_off + (uint32_t)(r0 + u) * p.rb_down, L, raw[u]);
         float acc[U][1];
 #pragma unroll
         for (int u = 0; u < U; u++) {
             acc[u][0] = 0.f;
             if (active && r0 + u < p.H) F::template dot<1>(raw[u], L, xt, acc[u]);
+        }
+        float resn[U];
+        if ((it + gridDim.x) * rpi < p.H) {
+            issue(it + gridDim.x);
+            fetch_res(it + gridDim.x, resn);
         }
         {
             float v[U];
@@ -1018,7 +1089,7 @@ __global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
             if (lig == 0) {
 #pragma unroll
                 for (int u = 0; u < U; u++)
-                    if (r0 + u < p.H) p.y[r0 + u] = moe_residual(p, r0 + u) + acc[u][0];
+                    if (r0 + u < p.H) p.y[r0 + u] = resv[u] + acc[u][0];
             }
         } else {
             if (lane == 0) {
@@ -1030,10 +1101,12 @@ __global__ void __launch_bounds__(512) moe_down_kernel(MoeParams p) {
                 float s = 0.f;
                 for (int w = 0; w < p.dn_S; w++) s += red[wave + w][lane];
                 const int64_t r = r0 + lane;
-                if (r < p.H) p.y[r] = moe_residual(p, r) + s;
+                if (r < p.H) p.y[r] = resv[0] + s;
             }
             __syncthreads();
         }
+#pragma unroll
+        for (int u = 0; u < U; u++) resv[u] = resn[u];
     }
 }
 

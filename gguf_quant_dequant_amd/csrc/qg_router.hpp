@@ -9,7 +9,8 @@ namespace qg {
 
 __global__ void __launch_bounds__(64) route_topk_kernel(const double *logits, int E, int k,
                                                         int *sel, float *w) {
-    route_topk_wave(logits, E, k, sel, w);
+    __shared__ RouteLds s_rt;
+    route_topk_wave(logits, E, k, sel, w, &s_rt);
 }
 
 // ------------------------------------------------------------------ MoE K1
