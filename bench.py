@@ -215,6 +215,19 @@ class Moe:
                        self.sel[t], self.w[t], self.ws, self.wsb)
 
 
+class MoeQ8(Moe):
+    """moe_ffn_q8act: the same chain with the expert GEMVs on int8 activations."""
+
+    def launch(self):
+        c = self.case
+        t = self.i % self.tokens
+        r, g, u, d = self.layers[self.i % len(self.layers)]
+        self.i += 1
+        self.q.moe_ffn_q8act(self.x[t], self.res[t], self.y[t], r, c.gate_fmt, g, c.up_fmt, u,
+                             c.down_fmt, d, c.hidden, c.n_experts, c.top_k, c.expert_dim,
+                             self.sel[t], self.w[t], self.ws, self.wsb)
+
+
 class MoeNorm(Moe):
     """The MoE FFN behind the fused residual add + RMSNorm (moe_ffn_norm):
     per token its own attention output and hidden state, one norm weight."""
@@ -445,18 +458,19 @@ ARITH = {
     "valu_q6k_int": "int8 codes x integer activations (rint at 2^21..2^22 of each 16-column "
                     "run's max), exact int32 sums, f32 per run",
     "mfma_f16": "f16 codes x f16 hi + lo activation parts on the matrix cores, f32 sums",
+    "mfma_bf16": "bf16 codes x bf16 hi + lo activation parts on the matrix cores, f32 sums",
     "q8act": "int8 codes x int8 activations (per 16 columns), exact int32 sums, f32 per group",
     "moe": "f64 router, f32 expert GEMVs on the vector ALUs",
+    "moe_q8": "f64 router, expert GEMVs as int8 codes x int8 activations (per 16 columns), "
+              "exact int32 sums, f32 per group",
     "read": "plain read, no arithmetic",
 }
 
 
-def gemv_arith(fmt, b, q8):
-    if q8:
-        return ARITH["q8act"]
-    if b == 1:
-        return ARITH["valu_q6k_int"] if fmt == 14 else ARITH["valu_f32"]
-    return ARITH["mfma_f16"]
+def gemv_arith(q):
+    """The arithmetic the library reports for its last GEMV call."""
+    return ARITH[{"valu_f32": "valu_f32", "valu_q6k_int": "valu_q6k_int", "mx_f16": "mfma_f16",
+                  "gemm_bf16": "mfma_bf16", "valu_q8act": "q8act"}[q.qg_last_kernel()]]
 
 
 def main():
@@ -486,7 +500,7 @@ def main():
             wall_gbs=round(args.steps * head.wbytes / wall / 1e9, 1),
             event_us_per_launch=round(per_us, 3),
             event_gbs=round(head.wbytes / (per_us * 1e-6) / 1e9, 1),
-            arith=ARITH["valu_f32"])
+            arith=gemv_arith(q))
         head_wall, head_us = wall, per_us
         del head
 
@@ -515,7 +529,7 @@ def main():
                 event_frac_hbm=round(w.wbytes / (per_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 3),
                 # multiply-adds of the product, as TFLOP/s (2 flops each)
                 tflops=round(2.0 * case.rows * case.cols * b / (per_us * 1e-6) / 1e12, 2),
-                arith=gemv_arith(case.fmt, b, q8))
+                arith=gemv_arith(q))
             del w
             torch.cuda.empty_cache()
         # the streaming floor: a plain read of the headline's and the lm_head's
@@ -556,6 +570,19 @@ def main():
                 tokens_per_s=round(1e6 / per_us, 1),
                 effective_gbs=round(m.bytes_per_token / (per_us * 1e-6) / 1e9, 1),
                 arith=ARITH["moe"])
+            del m
+        if not only or "moe_ffn_q8act_qwen3_30b_a3b" in only:
+            m = MoeQ8(synth.MOE_CASE, torch, q, args.moe_tokens)
+            steps = max(64, min(args.steps, 1000))
+            wall, ev_ms = time_launches(torch, m, steps, args.warmup, args.warm_seconds, scrub)
+            per_us = ev_ms * 1e3 / steps
+            results["moe_ffn_q8act_qwen3_30b_a3b"] = dict(
+                bytes_per_token=m.bytes_per_token, tokens=steps,
+                wall_tokens_per_s=round(steps / wall, 1),
+                event_us_per_token=round(per_us, 3),
+                tokens_per_s=round(1e6 / per_us, 1),
+                effective_gbs=round(m.bytes_per_token / (per_us * 1e-6) / 1e9, 1),
+                arith=ARITH["moe_q8"])
             del m
         if not only or "moe_ffn_norm_qwen3_30b_a3b" in only:
             m = MoeNorm(synth.MOE_CASE, torch, q, args.moe_tokens)

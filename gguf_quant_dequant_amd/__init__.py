@@ -32,11 +32,14 @@ SIGNATURES = {
     "qg_block_bytes": ([_INT], _INT),
     "qg_row_bytes": ([_INT, _I64], _I64),
     "qg_last_error": ([], ctypes.c_char_p),
+    "qg_last_kernel": ([], ctypes.c_char_p),
     "qgemv": ([_INT, _P, _I64, _I64, _P, _P, _INT, _P], _INT),
     "qgemv_q8act": ([_INT, _P, _I64, _I64, _P, _P, _P], _INT),
     "moe_ffn_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_size_t),
     "moe_ffn": ([_P, _P, _P, _P, _INT, _P, _INT, _P, _INT, _P, _I64, _I64, _I64, _I64,
                  _P, _P, _P, ctypes.c_size_t, _P], _INT),
+    "moe_ffn_q8act": ([_P, _P, _P, _P, _INT, _P, _INT, _P, _INT, _P, _I64, _I64, _I64, _I64,
+                       _P, _P, _P, ctypes.c_size_t, _P], _INT),
     "moe_ffn_noalloc": ([_P, _P, _P, _P, _INT, _P, _INT, _P, _INT, _P, _I64, _I64, _I64, _I64,
                          _P, _P, _P], _INT),
     "qg_route_topk": ([_P, _I64, _I64, _P, _P, _P], _INT),
@@ -119,6 +122,11 @@ def qg_last_error() -> str:
     return load_library().qg_last_error().decode()
 
 
+def qg_last_kernel() -> str:
+    """The arithmetic of the last successful qgemv / qgemv_q8act on this thread."""
+    return load_library().qg_last_kernel().decode()
+
+
 def qgemv(fmt: int, W, rows: int, cols: int, X, Y, batch: int, stream=None) -> None:
     """Y[b][r] = sum_c deq(W)[r][c] * X[b][c] on the GPU (see include/qgemv.h)."""
     rc = load_library().qgemv(fmt, _ptr(W), rows, cols, _ptr(X), _ptr(Y), batch,
@@ -143,6 +151,21 @@ def moe_ffn(x, residual, y, router, gate_fmt: int, gate, up_fmt: int, up, down_f
                                 _ptr(sel_weights), _ptr(workspace), workspace_bytes,
                                 _stream(stream))
     _check(rc, "moe_ffn")
+
+
+def moe_ffn_q8act(x, residual, y, router, gate_fmt: int, gate, up_fmt: int, up, down_fmt: int,
+                  down, hidden: int, n_experts: int, top_k: int, expert_dim: int,
+                  sel_experts=None, sel_weights=None, workspace=None,
+                  workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """moe_ffn with the expert GEMVs on int8-quantised activations (see include/qgemv.h)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    rc = load_library().moe_ffn_q8act(_ptr(x), _ptr(residual), _ptr(y), _ptr(router), gate_fmt,
+                                      _ptr(gate), up_fmt, _ptr(up), down_fmt, _ptr(down), hidden,
+                                      n_experts, top_k, expert_dim, _ptr(sel_experts),
+                                      _ptr(sel_weights), _ptr(workspace), workspace_bytes,
+                                      _stream(stream))
+    _check(rc, "moe_ffn_q8act")
 
 
 def moe_ffn_noalloc(x, residual, y, router, gate_fmt: int, gate, up_fmt: int, up,

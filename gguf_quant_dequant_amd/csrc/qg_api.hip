@@ -101,7 +101,7 @@ int moe_ffn_impl(const char *who, const float *x, const float *residual, float *
                  int down_fmt, const void *down, int64_t hidden, int64_t n_experts,
                  int64_t top_k, int64_t expert_dim, int32_t *sel_experts, float *sel_weights,
                  void *workspace, size_t workspace_bytes, void *stream, const NormStep *norm,
-                 int64_t tokens = 1) {
+                 int64_t tokens = 1, bool q8 = false) {
     if (tokens < 1) return fail(QG_EINVAL, "%s: tokens must be positive", who);
     if (tokens > kMaxTokens)
         return fail(QG_EUNSUPPORTED, "%s: tokens must be in 1..%d", who, kMaxTokens);
@@ -217,9 +217,10 @@ int moe_ffn_impl(const char *who, const float *x, const float *residual, float *
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_ELAUNCH, "%s: router launch failed: %s", who,
                                      hipGetErrorString(e));
-    int rc = tokens > 1 ? dispatch_gateup_tokens(gate_fmt, p, st) : dispatch_gateup(gate_fmt, p, st);
+    int rc = tokens > 1 ? dispatch_gateup_tokens(gate_fmt, p, st)
+                        : (q8 ? dispatch_gateup_q8(gate_fmt, p, st) : dispatch_gateup(gate_fmt, p, st));
     if (rc != QG_OK) return rc;
-    rc = dispatch_down(down_fmt, p, st);
+    rc = q8 ? dispatch_down_q8(down_fmt, p, st) : dispatch_down(down_fmt, p, st);
     if (rc != QG_OK) return rc;
     return ok();
 }
@@ -241,7 +242,10 @@ int64_t qg_row_bytes(int fmt, int64_t cols) {
 
 const char *qg_last_error(void) { return g_err; }
 
-// Batches above 8 run as groups of 8 (see qgemv).
+const char *qg_last_kernel(void) { return g_kernel; }
+
+// Block formats: batch >= 2 on the matrix cores in launches of up to 32
+// rows; F32 above 8 as groups of 8 (see qgemv).
 constexpr int kMaxBatch = 64;
 
 int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
@@ -269,7 +273,11 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
     hipStream_t st = (hipStream_t)stream;
     bool done = false;
     const int mrc = try_mx(fmt, W, rows, cols, X, Y, batch, rb, st, &done);
-    if (done) return mrc == QG_OK ? ok() : mrc;
+    if (done) {
+        if (mrc != QG_OK) return mrc;
+        g_kernel = "mx_f16";
+        return ok();
+    }
     if (fmt != QG_F32 && batch >= 2) {
         // block formats at batch >= 2: the batched matrix-core kernel, up to
         // 32 batch rows per launch (the weights are read once per launch)
@@ -281,6 +289,7 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
                                     : gemm_b<2>(fmt, W, rows, cols, Xb, Yb, nb, rb, st);
             if (rc != QG_OK) return rc;
         }
+        g_kernel = "gemm_bf16";
         return ok();
     }
     if (batch > 8) {
@@ -316,6 +325,7 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
         const int rc = dispatch_gemv(fmt, nb, aligned, cols, p, st);
         if (rc != QG_OK) return rc;
     }
+    g_kernel = (fmt == QG_Q6_K && batch == 1) ? "valu_q6k_int" : "valu_f32";
     return ok();
 }
 
@@ -350,7 +360,9 @@ int qgemv_q8act(int fmt, const void *W, int64_t rows, int64_t cols, const float 
     p.cols = (uint32_t)cols;
     p.batch_x = 1;
     const int rc = dispatch_gemv_q8(fmt, aligned_to(W, 4) && rb % 4 == 0, p, (hipStream_t)stream);
-    return rc == QG_OK ? ok() : rc;
+    if (rc != QG_OK) return rc;
+    g_kernel = "valu_q8act";
+    return ok();
 }
 
 size_t moe_ffn_workspace_bytes(int64_t n_experts, int64_t top_k, int64_t expert_dim) {
@@ -402,6 +414,16 @@ int moe_ffn(const float *x, const float *residual, float *y, const float *router
     return moe_ffn_impl("moe_ffn", x, residual, y, router, gate_fmt, gate, up_fmt, up, down_fmt,
                         down, hidden, n_experts, top_k, expert_dim, sel_experts, sel_weights,
                         workspace, workspace_bytes, stream, nullptr);
+}
+
+int moe_ffn_q8act(const float *x, const float *residual, float *y, const float *router,
+                  int gate_fmt, const void *gate, int up_fmt, const void *up, int down_fmt,
+                  const void *down, int64_t hidden, int64_t n_experts, int64_t top_k,
+                  int64_t expert_dim, int32_t *sel_experts, float *sel_weights, void *workspace,
+                  size_t workspace_bytes, void *stream) {
+    return moe_ffn_impl("moe_ffn_q8act", x, residual, y, router, gate_fmt, gate, up_fmt, up,
+                        down_fmt, down, hidden, n_experts, top_k, expert_dim, sel_experts,
+                        sel_weights, workspace, workspace_bytes, stream, nullptr, 1, true);
 }
 
 size_t moe_ffn_tokens_workspace_bytes(int64_t tokens, int64_t n_experts, int64_t top_k,

@@ -59,6 +59,9 @@ namespace qg {
 namespace host {
 
 inline thread_local char g_err[512] = "";
+// The arithmetic of the last qgemv / qgemv_q8act call on this thread that
+// enqueued work (qg_last_kernel).
+inline thread_local const char *g_kernel = "";
 
 inline int fail(int code, const char *fmt, ...) {
     va_list ap;
@@ -259,6 +262,8 @@ int gemm_b(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, f
 int dispatch_gateup(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_gateup_tokens(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_down(int fmt, const MoeParams &p, hipStream_t st);
+int dispatch_gateup_q8(int fmt, const MoeParams &p, hipStream_t st);
+int dispatch_down_q8(int fmt, const MoeParams &p, hipStream_t st);
 
 }  // namespace host
 }  // namespace qg

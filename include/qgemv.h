@@ -16,6 +16,8 @@
  *            routed on its own, the expert GEMVs grouped by expert.
  *   qgemv_q8act  qgemv at batch 1 on int8-quantised activations (integer
  *            dot products; the pages' lossy fast variant).
+ *   moe_ffn_q8act  moe_ffn with its expert GEMVs on int8-quantised
+ *            activations.
  *
  * Sources (web pages):
  *   docs.rs, crate ferrox-cuda 0.14.0, source src/gpu.rs -- block layouts
@@ -80,10 +82,14 @@ enum qg_status {
     QG_ELAUNCH = 3       /* the HIP runtime reported an error at launch */
 };
 
-/* Elements per block of fmt, or 0 for an unknown format. */
+/* Elements per block of fmt, or 0 for an unknown format: 32 for Q8_0 and
+ * Q4_0, 256 for the K-quants (the super-block of the gpu.rs page's
+ * *_MATVEC_KERNEL_SRC kernels), 1 for F32. */
 int qg_block_elems(int fmt);
 
-/* Bytes per block of fmt, or 0 for an unknown format. */
+/* Bytes per block of fmt, or 0 for an unknown format: Q8_0 34, Q4_0 18,
+ * Q4_K 144, Q5_K 176, Q6_K 210 (the block layouts of the same kernels),
+ * F32 4. */
 int qg_block_bytes(int fmt);
 
 /* Bytes of one row of cols elements: (cols / block_elems) * block_bytes,
@@ -93,8 +99,21 @@ int qg_block_bytes(int fmt);
 int64_t qg_row_bytes(int fmt, int64_t cols);
 
 /* Reason for the last non-QG_OK return on the calling thread ("" if none).
- * The string stays valid until the next call on the same thread. */
+ * Every refusal names its reason, as the aprender-serve page's `refuse`
+ * does for the resident MoE path.  The string stays valid until the next
+ * call on the same thread. */
 const char *qg_last_error(void);
+
+/* The arithmetic of the last qgemv or qgemv_q8act call on the calling
+ * thread that returned QG_OK ("" before any):
+ *   "valu_f32"      f32 products and sums on the vector ALUs;
+ *   "valu_q6k_int"  Q6_K at batch 1: integer activation digits, exact int32
+ *                   dot products, f32 per run (see qgemv);
+ *   "mx_f16"        matrix cores, f16 codes x f16 hi + lo activation parts;
+ *   "gemm_bf16"     matrix cores, bf16 codes x bf16 hi + lo activation parts;
+ *   "valu_q8act"    int8 codes x int8 activations (qgemv_q8act).
+ * A static string; reporting only, no effect on any call. */
+const char *qg_last_kernel(void);
 
 /*
  * qgemv: Y[b][r] = sum_c deq(W)[r][c] * X[b][c]   for b < batch, r < rows.
@@ -106,11 +125,11 @@ const char *qg_last_error(void);
  *   cols   > 0, a multiple of qg_block_elems(fmt).
  *   X      float [batch][cols], 4-byte aligned.
  *   Y      float [batch][rows], 4-byte aligned; must not overlap W or X.
- *   batch  1..64.  Up to 8, every weight byte is read from memory once and
- *          used for all batch rows (weight_matrix.rs apply_batch).  Above 8
- *          the rows run as groups of 8, one after another on the stream,
- *          and each group streams the weights again (prefill-sized batches;
- *          results per row as at batch <= 8).
+ *   batch  1..64.  Block formats: every weight byte is read from memory
+ *          once per launch and used for all batch rows of the launch
+ *          (weight_matrix.rs apply_batch); a launch takes up to 32 rows, so
+ *          batches of 33..64 read the weights twice.  F32: up to 8 rows per
+ *          launch, larger batches as groups of 8.
  *   stream hipStream_t or NULL.
  *
  * Dequantisation per element follows the block layouts of the gpu.rs page
@@ -123,10 +142,14 @@ const char *qg_last_error(void);
  * 1e-4 * sum|w x| unless a run's largest |x| exceeds its typical |x| by
  * more than ~400x where the weights meet the large values with small
  * codes).  At batch >= 2 (and for batch-1 rows wider than 512 lane tiles)
- * the block formats run on the matrix cores: codes are exact f16 values
- * (codes at a format's zero point are exact zeros), each 256-column chunk
- * of X is split into f16 hi + lo parts after a power-of-two scaling
- * (relative error < 2^-21 per element), sums are f32.  Results are
+ * the block formats run on the matrix cores with the codes as exact
+ * integers (codes at a format's zero point are exact zeros) and f32 sums:
+ * at batch 2..4 when the activations fit in LDS, and for the over-wide
+ * batch-1 rows, as f16 codes with each 256-column chunk of X split into
+ * f16 hi + lo parts after a power-of-two scaling (relative error < 2^-21
+ * per element); otherwise as bf16 codes with X split into bf16 hi + lo
+ * parts (relative error <= 2^-16 per element).  qg_last_kernel() names the
+ * arithmetic a call used.  Results are
  * deterministic run to run.  Limits: rows < 2^31, cols <= 65536; rows that fit neither
  * kernel (e.g. more than ~64 chunks of 256 columns at batch 1 beyond 512
  * lane tiles) return QG_EUNSUPPORTED.  Allocates nothing.
@@ -159,8 +182,9 @@ int qgemv_q8act(int fmt, const void *W, int64_t rows, int64_t cols,
                 const float *X, float *Y, void *stream);
 
 /* Bytes of caller-owned device workspace moe_ffn needs for these sizes
- * (f64 router logits, the k routes, the k SwiGLU activations).  Returns 0
- * for invalid sizes. */
+ * (f64 router logits, the k routes, the k SwiGLU activations): the
+ * per-layer device buffers of the aprender-serve page's `Scratch`, owned
+ * here by the caller.  Returns 0 for invalid sizes. */
 size_t moe_ffn_workspace_bytes(int64_t n_experts, int64_t top_k,
                                int64_t expert_dim);
 
@@ -300,6 +324,36 @@ int moe_ffn_norm(const float *attn_out, const float *hidden_in,
                  int64_t top_k, int64_t expert_dim, int32_t *sel_experts,
                  float *sel_weights, void *workspace, size_t workspace_bytes,
                  void *stream);
+
+/*
+ * moe_ffn_q8act: moe_ffn with the expert GEMVs on int8-quantised
+ * activations -- the pages' fast variant (gpu.rs page, module notes on the
+ * integer dp4a dot product; weight_matrix.rs page, cpu_int_dot_enabled)
+ * carried into the MoE chain, whose routing the aprender-serve page pins to
+ * the float kernels until its effect on the routes is measured
+ * (with_max_seq_len, the Q4kVariant / Q6kVariant pin).
+ *
+ *   The router GEMV, the routing and the residual add are moe_ffn's (the
+ *   router reads the unquantised x, so the routes of this call are
+ *   moe_ffn's bit for bit).  The gate and up GEMVs read x quantised as in
+ *   qgemv_q8act (groups of 16 columns, d = max|x| / 127, q = rint(x / d)
+ *   formed as x * (1 / d) in f32); the down GEMV reads each slot's f32
+ *   activations a[s] = w[s] * silu(g) * u quantised the same way.  Integer
+ *   code products summed exactly per group, one f32 multiply per group.
+ *   Versus moe_ffn the output moves by the quantisation of x (through g, u
+ *   and SwiGLU) and of a[s]: per row at most
+ *   sum_s sum_j |down[e_s][r][j]| * (|da[s][j]| + d_a[s][j] / 2), where da
+ *   is the change of a[s] that the gate/up quantisation causes.
+ *
+ *   Arguments, layouts, workspace (moe_ffn_workspace_bytes) and errors as
+ *   moe_ffn.  Allocates nothing.
+ */
+int moe_ffn_q8act(const float *x, const float *residual, float *y,
+                  const float *router, int gate_fmt, const void *gate,
+                  int up_fmt, const void *up, int down_fmt, const void *down,
+                  int64_t hidden, int64_t n_experts, int64_t top_k,
+                  int64_t expert_dim, int32_t *sel_experts, float *sel_weights,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * qg_route_topk: the routing step of moe_ffn on its own, on given logits

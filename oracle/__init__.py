@@ -81,6 +81,11 @@ def _load() -> ctypes.CDLL:
     lib.qref_moe_ffn.argtypes = [P, P, P, ci, P, ci, P, ci, P, i64, i64, i64, i64,
                                  P, P, P, P, P, P]
     lib.qref_moe_ffn.restype = ci
+    lib.qref_moe_q8act_bound.argtypes = [P, P, P, ci, P, ci, P, ci, P, i64, i64, i64, i64, P]
+    lib.qref_moe_q8act_bound.restype = ci
+    lib.qref_moe_ffn_q8act.argtypes = [P, P, P, ci, P, ci, P, ci, P, i64, i64, i64, i64,
+                                       ctypes.c_double, P, P, P, P, P]
+    lib.qref_moe_ffn_q8act.restype = ci
     _lib = lib
     return lib
 
@@ -277,3 +282,47 @@ def gemv_q8act(fmt: int, W: np.ndarray, rows: int, cols: int, X: np.ndarray):
     _check(_load().qref_gemv_q8act(fmt, _ptr(W), rows, cols, _ptr(X), batch, _ptr(Y), _ptr(A)),
            "gemv_q8act")
     return Y, A
+
+
+def moe_q8act_bound(x, residual, router, gate_fmt, gate, up_fmt, up, down_fmt, down,
+                    hidden, n_experts, top_k, expert_dim) -> np.ndarray:
+    """Per output row, the most the int8-activation MoE FFN may depart from
+    moe_ffn's exact y (quantisation of x and of the slots' activations,
+    propagated through gate/up, SwiGLU and down; see qref.c)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    residual = np.ascontiguousarray(residual, dtype=np.float32)
+    router = np.ascontiguousarray(router, dtype=np.float32)
+    gate = np.ascontiguousarray(gate).view(np.uint8).reshape(-1)
+    up = np.ascontiguousarray(up).view(np.uint8).reshape(-1)
+    down = np.ascontiguousarray(down).view(np.uint8).reshape(-1)
+    qb = np.empty(hidden, dtype=np.float64)
+    _check(_load().qref_moe_q8act_bound(_ptr(x), _ptr(residual), _ptr(router), gate_fmt,
+                                        _ptr(gate), up_fmt, _ptr(up), down_fmt, _ptr(down),
+                                        hidden, n_experts, top_k, expert_dim, _ptr(qb)),
+           "moe_q8act_bound")
+    return qb
+
+
+def moe_ffn_q8act(x, residual, router, gate_fmt, gate, up_fmt, up, down_fmt, down,
+                  hidden, n_experts, top_k, expert_dim, tie_window: float = 0.0) -> dict:
+    """The MoE FFN with its expert GEMVs on int8 activations (see qref.c).
+
+    Returns y[H], bound[H] (|residual| + sum |D aq|), tie[H] (the row's
+    sensitivity to one-step changes of codes within tie_window of a rounding
+    tie), sel[k], w[k]."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    residual = np.ascontiguousarray(residual, dtype=np.float32)
+    router = np.ascontiguousarray(router, dtype=np.float32)
+    gate = np.ascontiguousarray(gate).view(np.uint8).reshape(-1)
+    up = np.ascontiguousarray(up).view(np.uint8).reshape(-1)
+    down = np.ascontiguousarray(down).view(np.uint8).reshape(-1)
+    y = np.empty(hidden, dtype=np.float64)
+    bound = np.empty(hidden, dtype=np.float64)
+    tie = np.empty(hidden, dtype=np.float64)
+    sel = np.empty(top_k, dtype=np.int32)
+    w = np.empty(top_k, dtype=np.float64)
+    _check(_load().qref_moe_ffn_q8act(_ptr(x), _ptr(residual), _ptr(router), gate_fmt, _ptr(gate),
+                                      up_fmt, _ptr(up), down_fmt, _ptr(down), hidden, n_experts,
+                                      top_k, expert_dim, float(tie_window), _ptr(y), _ptr(bound),
+                                      _ptr(tie), _ptr(sel), _ptr(w)), "moe_ffn_q8act")
+    return dict(y=y, bound=bound, tie=tie, sel=sel, w=w)

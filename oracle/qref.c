@@ -579,3 +579,217 @@ done:
     free(w); free(xq); free(q); free(d);
     return rc;
 }
+
+/* Bound on how far the int8-activation MoE FFN may depart from the exact
+ * one (qref_moe_ffn), per output row.  The variant quantises x, and each
+ * slot's f32 SwiGLU activations, per group of 16 columns with the step
+ * d = max|v| / 127, so every quantised value is within d / 2 of its input
+ * (weight_matrix.rs page, cpu_int_dot_enabled: int8 activations; the group
+ * and scale are the reading stated in qref_quantize_q8).  Propagated through
+ * the chain of qref_moe_ffn (routes unchanged: the router reads x itself):
+ *   dg_j <= sum_c |G_jc| d_x(c) / 2 + 1e-5 sum_c |G_jc x_c|, du_j alike;
+ *   da_j <= w (|silu(g_j)| + L dg_j) du_j + w L dg_j |u_j| + 1e-5 |a_j|,
+ *           L = 1.1 >= max |silu'|;
+ *   the slot's group step as the variant forms it is at most
+ *   dq = (max over the group of |a_j| + da_j) / 127;
+ *   |dy_r| <= sum_s sum_j |D_rj| (da_j + dq / 2).
+ * The 1e-5 terms cover the f32 sums of g, u and a; every half step is
+ * widened by 1e-3 for the f32 arithmetic that forms the codes.  A
+ * non-finite x gives NaN bounds. */
+int qref_moe_q8act_bound(const float *x, const float *residual, const float *router,
+                         int gate_fmt, const void *gate, int up_fmt, const void *up,
+                         int down_fmt, const void *down, int64_t hidden, int64_t n_experts,
+                         int64_t top_k, int64_t expert_dim, double *qbound) {
+    const double half = 0.5 * (1.0 + 1e-3), L = 1.1;
+    int64_t H = hidden, E = n_experts, K = top_k, F = expert_dim;
+    int64_t rb_g = qref_row_bytes(gate_fmt, H), rb_u = qref_row_bytes(up_fmt, H);
+    int64_t rb_d = qref_row_bytes(down_fmt, F);
+    int64_t e, s, j, r, c;
+    int rc = QREF_OK;
+    double *logits = NULL, *w = NULL, *row = NULL, *dx = NULL, *da = NULL, *dq = NULL;
+    int32_t *sel = NULL;
+    if (!x || !residual || !router || !gate || !up || !down || !qbound) return QREF_EINVAL;
+    if (H <= 0 || E <= 0 || K <= 0 || F <= 0 || K > E || H % 16 || F % 16) return QREF_EINVAL;
+    if (rb_g < 0 || rb_u < 0 || rb_d < 0) return QREF_EUNSUPPORTED;
+    logits = (double *)malloc(sizeof(double) * (size_t)E);
+    w = (double *)malloc(sizeof(double) * (size_t)K);
+    sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    row = (double *)malloc(sizeof(double) * (size_t)(H > F ? H : F));
+    dx = (double *)malloc(sizeof(double) * (size_t)H);
+    da = (double *)malloc(sizeof(double) * (size_t)(K * F));
+    dq = (double *)malloc(sizeof(double) * (size_t)(K * F));
+    if (!logits || !w || !sel || !row || !dx || !da || !dq) { rc = QREF_EINVAL; goto done; }
+
+    /* the group step of x at every column */
+    for (c = 0; c < H; c += 16) {
+        double amax = 0.0;
+        for (j = 0; j < 16; j++) {
+            double a = fabs((double)x[c + j]);
+            amax = (a > amax || a != a) ? a : amax;
+        }
+        for (j = 0; j < 16; j++) dx[c + j] = amax / 127.0;
+    }
+    for (e = 0; e < E; e++) {
+        double yabs;
+        rc = qref_dequant_row(QREF_F32, (const uint8_t *)router + e * H * 4, H, row);
+        if (rc) goto done;
+        dot_f64(row, x, H, &logits[e], &yabs);
+    }
+    rc = qref_route(logits, (int)E, (int)K, sel, w);
+    if (rc) goto done;
+
+    for (s = 0; s < K; s++) {
+        const uint8_t *gb = (const uint8_t *)gate + (int64_t)sel[s] * F * rb_g;
+        const uint8_t *ub = (const uint8_t *)up + (int64_t)sel[s] * F * rb_u;
+        for (j = 0; j < F; j++) {
+            double g = 0, u = 0, gs = 0, us = 0, ga = 0, ua = 0, a, dg, du;
+            rc = qref_dequant_row(gate_fmt, gb + j * rb_g, H, row);
+            if (rc) goto done;
+            for (c = 0; c < H; c++) {
+                g += row[c] * (double)x[c];
+                gs += fabs(row[c]) * dx[c];
+                ga += fabs(row[c] * (double)x[c]);
+            }
+            rc = qref_dequant_row(up_fmt, ub + j * rb_u, H, row);
+            if (rc) goto done;
+            for (c = 0; c < H; c++) {
+                u += row[c] * (double)x[c];
+                us += fabs(row[c]) * dx[c];
+                ua += fabs(row[c] * (double)x[c]);
+            }
+            dg = half * gs + 1e-5 * ga;
+            du = half * us + 1e-5 * ua;
+            a = w[s] * qref_silu(g) * u;
+            da[s * F + j] = w[s] * (fabs(qref_silu(g)) + L * dg) * du + w[s] * L * dg * fabs(u) +
+                            1e-5 * fabs(a);
+            dq[s * F + j] = fabs(a);  /* |a|, turned into the group step below */
+        }
+        for (j = 0; j < F; j += 16) {
+            double m = 0.0;
+            int64_t t;
+            for (t = 0; t < 16; t++) {
+                double v = dq[s * F + j + t] + da[s * F + j + t];
+                m = (v > m || v != v) ? v : m;
+            }
+            for (t = 0; t < 16; t++) dq[s * F + j + t] = m / 127.0;
+        }
+    }
+    for (r = 0; r < H; r++) {
+        double b = 0.0;
+        for (s = 0; s < K; s++) {
+            const uint8_t *db = (const uint8_t *)down + (int64_t)sel[s] * H * rb_d;
+            rc = qref_dequant_row(down_fmt, db + r * rb_d, F, row);
+            if (rc) goto done;
+            for (j = 0; j < F; j++)
+                b += fabs(row[j]) * (da[s * F + j] + half * dq[s * F + j]);
+        }
+        qbound[r] = b;
+    }
+done:
+    free(logits); free(w); free(sel); free(row); free(dx); free(da); free(dq);
+    return rc;
+}
+
+/* The int8-activation MoE FFN (the MoE chain of qref_moe_ffn with the
+ * expert GEMVs on int8 activations; weight_matrix.rs page,
+ * cpu_int_dot_enabled; grouping and scale as qref_quantize_q8):
+ *   logits, (sel, w)  as qref_moe_ffn (the router reads x itself);
+ *   xq = q d from qref_quantize_q8(x);  g = G xq,  u = U xq  (f64);
+ *   a[s] = (float)(w_s silu(g) u), the f32 vector the down GEMV reads;
+ *   aq[s] = q d from qref_quantize_q8(a[s]);
+ *   y = residual + sum_s D aq[s]   (f64, slots in rank order);
+ *   bound[r] = |residual[r]| + sum_s sum_j |D_rj aq_j|.
+ * tie[r] (may be NULL): sum of |D_rj| d over the slot elements whose scaled
+ * value a / d lies within `window` of a rounding tie (an integer + 1/2) --
+ * the most that a one-step change of those codes, as another f32 rounding
+ * of a could cause, moves row r. */
+int qref_moe_ffn_q8act(const float *x, const float *residual, const float *router,
+                       int gate_fmt, const void *gate, int up_fmt, const void *up,
+                       int down_fmt, const void *down, int64_t hidden, int64_t n_experts,
+                       int64_t top_k, int64_t expert_dim, double window, double *y,
+                       double *bound, double *tie, int32_t *sel_out, double *w_out) {
+    int64_t H = hidden, E = n_experts, K = top_k, F = expert_dim;
+    int64_t rb_g = qref_row_bytes(gate_fmt, H), rb_u = qref_row_bytes(up_fmt, H);
+    int64_t rb_d = qref_row_bytes(down_fmt, F);
+    int64_t e, s, j, r, c;
+    int rc = QREF_OK;
+    double *logits = NULL, *w = NULL, *row = NULL, *xq = NULL, *aq = NULL, *near = NULL;
+    float *a = NULL, *d = NULL;
+    int8_t *q = NULL;
+    int32_t *sel = NULL;
+    if (!x || !residual || !router || !gate || !up || !down || !y) return QREF_EINVAL;
+    if (H <= 0 || E <= 0 || K <= 0 || F <= 0 || K > E || H % 16 || F % 16) return QREF_EINVAL;
+    if (rb_g < 0 || rb_u < 0 || rb_d < 0) return QREF_EUNSUPPORTED;
+    logits = (double *)malloc(sizeof(double) * (size_t)E);
+    w = (double *)malloc(sizeof(double) * (size_t)K);
+    sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)K);
+    row = (double *)malloc(sizeof(double) * (size_t)(H > F ? H : F));
+    xq = (double *)malloc(sizeof(double) * (size_t)H);
+    aq = (double *)malloc(sizeof(double) * (size_t)(K * F));
+    near = (double *)malloc(sizeof(double) * (size_t)(K * F));
+    a = (float *)malloc(sizeof(float) * (size_t)F);
+    q = (int8_t *)malloc((size_t)(H > F ? H : F));
+    d = (float *)malloc(sizeof(float) * (size_t)((H > F ? H : F) / 16));
+    if (!logits || !w || !sel || !row || !xq || !aq || !near || !a || !q || !d) {
+        rc = QREF_EINVAL;
+        goto done;
+    }
+    for (e = 0; e < E; e++) {
+        double yabs;
+        rc = qref_dequant_row(QREF_F32, (const uint8_t *)router + e * H * 4, H, row);
+        if (rc) goto done;
+        dot_f64(row, x, H, &logits[e], &yabs);
+    }
+    rc = qref_route(logits, (int)E, (int)K, sel, w);
+    if (rc) goto done;
+    rc = qref_quantize_q8(x, H, q, d);
+    if (rc) goto done;
+    for (c = 0; c < H; c++) xq[c] = (double)q[c] * (double)d[c / 16];
+
+    for (s = 0; s < K; s++) {
+        const uint8_t *gb = (const uint8_t *)gate + (int64_t)sel[s] * F * rb_g;
+        const uint8_t *ub = (const uint8_t *)up + (int64_t)sel[s] * F * rb_u;
+        for (j = 0; j < F; j++) {
+            double g = 0.0, u = 0.0;
+            rc = qref_dequant_row(gate_fmt, gb + j * rb_g, H, row);
+            if (rc) goto done;
+            for (c = 0; c < H; c++) g += row[c] * xq[c];
+            rc = qref_dequant_row(up_fmt, ub + j * rb_u, H, row);
+            if (rc) goto done;
+            for (c = 0; c < H; c++) u += row[c] * xq[c];
+            a[j] = (float)(w[s] * qref_silu(g) * u);
+        }
+        rc = qref_quantize_q8(a, F, q, d);
+        if (rc) goto done;
+        for (j = 0; j < F; j++) {
+            const double dj = (double)d[j / 16];
+            const double t = dj > 0.0 ? (double)a[j] / dj : 0.0;
+            const double frac = t - floor(t);
+            aq[s * F + j] = (double)q[j] * dj;
+            near[s * F + j] = fabs(frac - 0.5) < window ? dj : 0.0;
+        }
+    }
+    for (r = 0; r < H; r++) {
+        double acc = (double)residual[r], aabs = fabs((double)residual[r]), tb = 0.0;
+        for (s = 0; s < K; s++) {
+            const uint8_t *db = (const uint8_t *)down + (int64_t)sel[s] * H * rb_d;
+            rc = qref_dequant_row(down_fmt, db + r * rb_d, F, row);
+            if (rc) goto done;
+            for (j = 0; j < F; j++) {
+                double p = row[j] * aq[s * F + j];
+                acc += p;
+                aabs += fabs(p);
+                tb += fabs(row[j]) * near[s * F + j];
+            }
+        }
+        y[r] = acc;
+        if (bound) bound[r] = aabs;
+        if (tie) tie[r] = tb;
+    }
+    if (sel_out) memcpy(sel_out, sel, sizeof(int32_t) * (size_t)K);
+    if (w_out) memcpy(w_out, w, sizeof(double) * (size_t)K);
+done:
+    free(logits); free(w); free(sel); free(row); free(xq); free(aq); free(near);
+    free(a); free(q); free(d);
+    return rc;
+}
