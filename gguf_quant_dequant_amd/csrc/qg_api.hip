@@ -211,8 +211,9 @@ int moe_ffn_impl(const char *who, const float *x, const float *residual, float *
                            router, x, (int)tokens, (int)hidden, (int)n_experts,
                            (double *)(ws + wl.logits));
     } else {
-        hipLaunchKernelGGL(moe_router_kernel, dim3((unsigned)n_experts), dim3(64), 0, st, router,
-                           x, (int)hidden, (double *)(ws + wl.logits));
+        hipLaunchKernelGGL(moe_router_kernel<QG_ROUTER_WAVES>, dim3((unsigned)n_experts),
+                           dim3(64 * QG_ROUTER_WAVES), 0, st, router, x, (int)hidden,
+                           (double *)(ws + wl.logits));
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_ELAUNCH, "%s: router launch failed: %s", who,

@@ -54,6 +54,10 @@
 #ifndef QG_MOE_DN_T128
 #define QG_MOE_DN_T128 0
 #endif
+// Waves per expert row in the MoE router kernel (1, 2, 4 or 8).
+#ifndef QG_ROUTER_WAVES
+#define QG_ROUTER_WAVES 1
+#endif
 
 namespace qg {
 namespace host {

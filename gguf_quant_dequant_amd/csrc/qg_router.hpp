@@ -16,23 +16,35 @@ __global__ void __launch_bounds__(64) route_topk_kernel(const double *logits, in
 // ------------------------------------------------------------------ MoE K1
 
 // logits[e] = sum_i R[e][i] * x[i]: every f32*f32 product is exact in f64
-// and the sum is f64 with a fixed tree.  One wave per expert row.
-__global__ void __launch_bounds__(64) moe_router_kernel(const float *__restrict__ R,
-                                                        const float *__restrict__ x, int H,
-                                                        double *__restrict__ logits) {
-    const int e = blockIdx.x, lane = threadIdx.x;
+// and the sum is f64 in a fixed order.  One workgroup of RW waves per
+// expert row: wave w takes the w-th of RW equal column ranges (whole
+// multiples of 256 columns) in rounds of 2048 columns, all loads of a round
+// issued before its FMAs, reduces across its lanes with a fixed tree, and
+// the RW partial sums are added in wave order.  RW = 1 (one wave per
+// expert) is the default: spreading the 128-expert router's rows over 2, 4
+// or 8 waves made the MoE chain slower (21.6 -> 21.7 / 21.9 / 22.1 us per
+// token), so the router's time is not its per-wave chain of loads and FMAs.
+template <int RW>
+__global__ void __launch_bounds__(64 * RW) moe_router_kernel(const float *__restrict__ R,
+                                                             const float *__restrict__ x, int H,
+                                                             double *__restrict__ logits) {
+    __shared__ double part[RW];
+    const int e = blockIdx.x, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const rsrc_t rr = make_rsrc(R + (int64_t)e * H, 4u * (uint32_t)H);
     const rsrc_t rx = make_rsrc(x, 4u * (uint32_t)H);
+    const int hw = (H + 256 * RW - 1) / (256 * RW) * 256;  // columns per wave
+    const int cb = wave * hw, ce = cb + hw < H ? cb + hw : H;
     double acc = 0.0;
-    // 2048 columns per round, all loads of a round issued before its FMAs;
-    // columns past H read as zero through the resources
-    for (int c0 = 0; c0 < H; c0 += 2048) {
+    // columns past H (and past the wave's range) read as zero through the
+    // resources, or are skipped by the guard below
+    for (int c0 = cb; c0 < ce; c0 += 2048) {
         uint32_t a[8][4], b[8][4];
 #pragma unroll
         for (int i = 0; i < 8; i++) {
             const int c = c0 + 256 * i + 4 * lane;
-            load_dw<4, QG_ROUTER_AUX>(rr, 4u * c, a[i]);
-            load_dw<4>(rx, 4u * c, b[i]);
+            const uint32_t off = c < ce ? 4u * (uint32_t)c : 0xFFFFFFF0u;
+            load_dw<4, QG_ROUTER_AUX>(rr, off, a[i]);
+            load_dw<4>(rx, off, b[i]);
         }
 #pragma unroll
         for (int i = 0; i < 8; i++)
@@ -42,7 +54,14 @@ __global__ void __launch_bounds__(64) moe_router_kernel(const float *__restrict_
                           (double)__builtin_bit_cast(float, b[i][j]), acc);
     }
     acc = wave_sum_d(acc);
-    if (lane == 0) logits[e] = acc;
+    if (lane == 0) part[wave] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        double sum = part[0];
+#pragma unroll
+        for (int w = 1; w < RW; w++) sum += part[w];
+        logits[e] = sum;
+    }
 }
 
 // ------------------------------------------------------- MoE K1, with norm
