@@ -47,12 +47,6 @@ struct GemvParams {
     int32_t G;           // row groups per workgroup
 };
 
-// Buffer resource for the weight bytes from byte `start` of W to the end
-// (w_bytes): base rounded down to 4 bytes, *delta = bytes between that base
-// and W + start.  The record count is rounded up to a whole dword: a dword
-// that only partly overlaps the array is read whole (its other bytes lie in
-// the same page), while the hardware returns zero for a dword that overlaps
-// the record range only in part.
 // Row offset of a load that is not wanted: every resource built by
 // rows_rsrc ends at or below it, so the load reads zeros and touches no
 // memory.  Loads under a branch would wait for each other (a realigning
@@ -60,6 +54,12 @@ struct GemvParams {
 // so unwanted rows are loaded from here instead of being skipped.
 constexpr uint32_t kOorRow = 0xFFFF0000u;
 
+// Buffer resource for the weight bytes from byte `start` of W to the end
+// (w_bytes): base rounded down to 4 bytes, *delta = bytes between that base
+// and W + start.  The record count is rounded up to a whole dword: a dword
+// that only partly overlaps the array is read whole (its other bytes lie in
+// the same page), while the hardware returns zero for a dword that overlaps
+// the record range only in part.
 __device__ __forceinline__ rsrc_t rows_rsrc(const uint8_t *W, uint64_t w_bytes, uint64_t start,
                                             uint32_t *delta) {
     const uint8_t *base = W + start;
