@@ -196,6 +196,7 @@ int moe_ffn_impl(const char *who, const float *x, const float *residual, float *
     p.w_out = sel_weights;
 
     hipStream_t st = (hipStream_t)stream;
+    if (const int rc0 = no_pending_error(who)) return rc0;
     if (norm) {
         // x = attn_out, residual = hidden_in: the router kernel forms
         // h = x + residual and its norm, the experts read xn (workspace),
@@ -272,6 +273,7 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
         return fail(QG_EUNSUPPORTED, "qgemv: F32 rows must be a multiple of 4 floats");
     const int64_t rb = qg_row_bytes(fmt, cols);
     hipStream_t st = (hipStream_t)stream;
+    if (const int rc0 = no_pending_error("qgemv")) return rc0;
     bool done = false;
     const int mrc = try_mx(fmt, W, rows, cols, X, Y, batch, rb, st, &done);
     if (done) {
@@ -360,6 +362,7 @@ int qgemv_q8act(int fmt, const void *W, int64_t rows, int64_t cols, const float 
     p.row_bytes = (uint32_t)rb;
     p.cols = (uint32_t)cols;
     p.batch_x = 1;
+    if (const int rc0 = no_pending_error("qgemv_q8act")) return rc0;
     const int rc = dispatch_gemv_q8(fmt, aligned_to(W, 4) && rb % 4 == 0, p, (hipStream_t)stream);
     if (rc != QG_OK) return rc;
     g_kernel = "valu_q8act";
@@ -382,6 +385,7 @@ int qg_route_topk(const double *logits, int64_t n_experts, int64_t top_k, int32_
                     kMaxExperts, kMaxTopK);
     if (!aligned_to(logits, 8) || !aligned_to(sel_experts, 4) || !aligned_to(sel_weights, 4))
         return fail(QG_EINVAL, "qg_route_topk: misaligned pointer");
+    if (const int rc0 = no_pending_error("qg_route_topk")) return rc0;
     hipLaunchKernelGGL(route_topk_kernel, dim3(1), dim3(64), 0, (hipStream_t)stream, logits,
                        (int)n_experts, (int)top_k, (int *)sel_experts, sel_weights);
     const hipError_t e = hipGetLastError();
@@ -399,6 +403,7 @@ int qg_stream_read(const void *buf, size_t bytes, uint32_t *out, int grid, void 
     const uint64_t need = (bytes + per_wg - 1) / per_wg;
     if (grid <= 0) grid = (int)(need < 2048 ? need : 2048);
     if ((uint64_t)grid > need) grid = (int)need;
+    if (const int rc0 = no_pending_error("qg_stream_read")) return rc0;
     hipLaunchKernelGGL(stream_read_kernel, dim3((unsigned)grid), dim3(kStreamThreads), 0,
                        (hipStream_t)stream, (const uint8_t *)buf, (uint64_t)bytes, out);
     const hipError_t e = hipGetLastError();

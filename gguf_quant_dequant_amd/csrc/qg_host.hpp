@@ -80,6 +80,19 @@ inline int ok() {
     return QG_OK;
 }
 
+// Called by every entry point after its validation, before its first
+// launch: an error the HIP runtime still holds from earlier work on this
+// thread is reported (and thereby cleared) as that, with nothing launched,
+// instead of surfacing after this call's launch as if the launch had failed.
+inline int no_pending_error(const char *who) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(QG_ELAUNCH, "%s: nothing launched: the HIP runtime holds an error from earlier "
+                                "work on this thread: %s",
+                    who, hipGetErrorString(e));
+    return QG_OK;
+}
+
 struct Geom {
     int elems, bytes;
 };

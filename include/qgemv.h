@@ -79,7 +79,10 @@ enum qg_status {
     QG_EUNSUPPORTED = 2, /* an unknown format, cols not a multiple of the
                             block size, batch outside 1..8, a size beyond the
                             kernels' limits, a router that is not F32 */
-    QG_ELAUNCH = 3       /* the HIP runtime reported an error at launch */
+    QG_ELAUNCH = 3       /* the HIP runtime reported an error at launch, or
+                            still held one from earlier work on the calling
+                            thread when the call was about to launch (then
+                            nothing is launched; the error is cleared) */
 };
 
 /* Elements per block of fmt, or 0 for an unknown format: 32 for Q8_0 and
