@@ -457,6 +457,8 @@ ARITH = {
     "valu_f32": "f32 products and sums on the vector ALUs",
     "valu_q6k_int": "int8 codes x integer activations (rint at 2^21..2^22 of each 16-column "
                     "run's max), exact int32 sums, f32 per run",
+    "mfma_i8_q6k": "int8 codes x integer activations (rint at 2^21..2^22 of each 16-column "
+                   "run's max) on the matrix cores, exact int32 sums, f32 per run",
     "mfma_f16": "f16 codes x f16 hi + lo activation parts on the matrix cores, f32 sums",
     "mfma_bf16": "bf16 codes x bf16 hi + lo activation parts on the matrix cores, f32 sums",
     "q8act": "int8 codes x int8 activations (per 16 columns), exact int32 sums, f32 per group",
@@ -469,8 +471,9 @@ ARITH = {
 
 def gemv_arith(q):
     """The arithmetic the library reports for its last GEMV call."""
-    return ARITH[{"valu_f32": "valu_f32", "valu_q6k_int": "valu_q6k_int", "mx_f16": "mfma_f16",
-                  "gemm_bf16": "mfma_bf16", "valu_q8act": "q8act"}[q.qg_last_kernel()]]
+    return ARITH[{"valu_f32": "valu_f32", "valu_q6k_int": "valu_q6k_int",
+                  "mfma_i8_q6k": "mfma_i8_q6k", "mx_f16": "mfma_f16", "gemm_bf16": "mfma_bf16",
+                  "valu_q8act": "q8act"}[q.qg_last_kernel()]]
 
 
 def main():

@@ -275,6 +275,23 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
     hipStream_t st = (hipStream_t)stream;
     if (const int rc0 = no_pending_error("qgemv")) return rc0;
     bool done = false;
+    if (QG_Q6_MX && fmt == QG_Q6_K && batch == 1) {
+        GemvParams p{};
+        p.W = (const uint8_t *)W;
+        p.X = X;
+        p.Y = Y;
+        p.rows = rows;
+        p.w_bytes = (uint64_t)rows * (uint64_t)rb;
+        p.row_bytes = (uint32_t)rb;
+        p.cols = (uint32_t)cols;
+        p.batch_x = 1;
+        const int qrc = try_q6mx(p, st, &done);
+        if (done) {
+            if (qrc != QG_OK) return qrc;
+            g_kernel = "mfma_i8_q6k";
+            return ok();
+        }
+    }
     const int mrc = try_mx(fmt, W, rows, cols, X, Y, batch, rb, st, &done);
     if (done) {
         if (mrc != QG_OK) return mrc;

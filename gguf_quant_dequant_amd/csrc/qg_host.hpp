@@ -58,6 +58,11 @@
 #ifndef QG_ROUTER_WAVES
 #define QG_ROUTER_WAVES 1
 #endif
+// 1: batch-1 Q6_K rows of up to 4096 columns run on the matrix cores
+// (int8 digit-plane products, qg_q6mx.hpp); 0: on the VALU kernel.
+#ifndef QG_Q6_MX
+#define QG_Q6_MX 1
+#endif
 
 namespace qg {
 namespace host {
@@ -281,6 +286,7 @@ int dispatch_gateup_tokens(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_down(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_gateup_q8(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_down_q8(int fmt, const MoeParams &p, hipStream_t st);
+int try_q6mx(const GemvParams &p, hipStream_t st, bool *done);
 
 }  // namespace host
 }  // namespace qg

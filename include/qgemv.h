@@ -112,6 +112,8 @@ const char *qg_last_error(void);
  *   "valu_f32"      f32 products and sums on the vector ALUs;
  *   "valu_q6k_int"  Q6_K at batch 1: integer activation digits, exact int32
  *                   dot products, f32 per run (see qgemv);
+ *   "mfma_i8_q6k"   the same arithmetic with the int32 products on the
+ *                   matrix cores (Q6_K batch-1 rows of up to 4096 columns);
  *   "mx_f16"        matrix cores, f16 codes x f16 hi + lo activation parts;
  *   "gemm_bf16"     matrix cores, bf16 codes x bf16 hi + lo activation parts;
  *   "valu_q8act"    int8 codes x int8 activations (qgemv_q8act).
@@ -144,7 +146,10 @@ const char *qg_last_kernel(void);
  * most 2^-22 * max|x| * sum|w| over the run (within the tolerance
  * 1e-4 * sum|w x| unless a run's largest |x| exceeds its typical |x| by
  * more than ~400x where the weights meet the large values with small
- * codes).  At batch >= 2 (and for batch-1 rows wider than 512 lane tiles)
+ * codes); rows of 256..2048 columns (any multiple of 256) or of 512..4096
+ * (any multiple of 512) form those int32 products on the matrix cores
+ * (v_mfma_i32_16x16x64_i8, 16 weight rows per instruction), the same sums
+ * bit for bit in int32.  At batch >= 2 (and for batch-1 rows wider than 512 lane tiles)
  * the block formats run on the matrix cores with the codes as exact
  * integers (codes at a format's zero point are exact zeros) and f32 sums:
  * at batch 2..4 when the activations fit in LDS, and for the over-wide
