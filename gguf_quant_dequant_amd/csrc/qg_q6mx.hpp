@@ -73,6 +73,57 @@ __device__ __forceinline__ void digits4(const float (&x)[4], uint32_t mb, uint32
     pl[2] = __builtin_amdgcn_perm(e, c, 0x05040100u);
 }
 
+// A lane's fields of one tile of its row (staged in LDS): the two ql
+// dwords and the qh dword as two aligned dwords each with their realigning
+// selector, and d * sc / 4 of the lane's group (the codes carry a factor 4).
+struct Fields {
+    uint32_t a0, a1, b0, b1, h0, h1, sel;
+    float ds;
+};
+
+// Tile i of wave `wave` (super-block wave * TPW / 4 + i / 4, half (i / 2) %
+// 2, l0 = 16 (i % 2)) of the row staged at byte `rowoff`; the lane's code
+// bytes start 4kg bytes into each field.  Staged bytes keep their offset
+// mod 4, so a field at 2 mod 4 is realigned from two dwords.
+template <int TPW>
+__device__ __forceinline__ void fetch(const uint32_t *stage, uint32_t rowoff, int wave, int kg,
+                                      int i, Fields &f) {
+    const int sb = wave * (TPW / 4) + (i >> 2), h = (i >> 1) & 1, l0 = (i & 1) * 16;
+    const uint32_t blk = rowoff + 210u * (uint32_t)sb;
+    const uint32_t qoff = blk + 4u * (uint32_t)kg;
+    const uint32_t *q = stage + (qoff >> 2);
+    const int fa = (64 * h + l0) / 4;         // ql, groups 0 and 2
+    const int fb = fa + 8;                    // ql, groups 1 and 3
+    const int fh = (128 + 32 * h + l0) / 4;   // qh
+    f.a0 = q[fa];
+    f.a1 = q[fa + 1];
+    f.b0 = q[fb];
+    f.b1 = q[fb + 1];
+    f.h0 = q[fh];
+    f.h1 = q[fh + 1];
+    f.sel = (qoff & 2u) ? 0x05040302u : 0x03020100u;
+    // d and the sub-block scale sc[8h + 2kg + l0 / 16] of row n, group kg
+    const int8_t *st8 = reinterpret_cast<const int8_t *>(stage);
+    const float sc = (float)st8[blk + 2u * (uint32_t)kg + (uint32_t)(192 + 8 * h + l0 / 16)];
+    const float d = (float)*reinterpret_cast<const _Float16 *>(st8 + blk + 208u);
+    f.ds = d * 0.25f * sc;
+}
+
+// The codes 4(q - 32) of the lane's four groups as signed bytes: low four
+// bits to bits 2..5, the two top bits to bits 6..7 with the upper one
+// flipped.
+__device__ __forceinline__ v4i codes(const Fields &f) {
+    const uint32_t qa = __builtin_amdgcn_perm(f.a1, f.a0, f.sel);
+    const uint32_t qb = __builtin_amdgcn_perm(f.b1, f.b0, f.sel);
+    const uint32_t hx = __builtin_amdgcn_perm(f.h1, f.h0, f.sel) ^ 0xAAAAAAAAu;
+    v4i B;
+    B[0] = (int)(((qa << 2) & 0x3C3C3C3Cu) | ((hx << 6) & 0xC0C0C0C0u));
+    B[1] = (int)(((qb << 2) & 0x3C3C3C3Cu) | ((hx << 4) & 0xC0C0C0C0u));
+    B[2] = (int)(((qa >> 2) & 0x3C3C3C3Cu) | ((hx << 2) & 0xC0C0C0C0u));
+    B[3] = (int)(((qb >> 2) & 0x3C3C3C3Cu) | (hx & 0xC0C0C0C0u));
+    return B;
+}
+
 template <int TPW>
 __global__ void __launch_bounds__(512) q6k_mx1_kernel(GemvParams p) {
     extern __shared__ __attribute__((aligned(16))) uint32_t stage[];
@@ -130,7 +181,6 @@ __global__ void __launch_bounds__(512) q6k_mx1_kernel(GemvParams p) {
     }
     __syncthreads();
 
-    const int8_t *st8 = reinterpret_cast<const int8_t *>(stage);
     const v4i zero = {0, 0, 0, 0};
     for (; it * kRows < p.rows; it += gridDim.x) {
         // every wave has finished reading the previous block (the barrier
@@ -144,36 +194,19 @@ __global__ void __launch_bounds__(512) q6k_mx1_kernel(GemvParams p) {
         }
         const uint32_t rowoff = d16 + (uint32_t)n * p.row_bytes;
         float acc = 0.f;
+        // tile i's fields, read one tile ahead of its instruction; a
+        // tile's scaling waits for the next tile's instruction to issue
+        Fields fd[TPW];
+        fetch<TPW>(stage, rowoff, wave, kg, 0, fd[0]);
+        v4i Dp = zero;
 #pragma unroll
         for (int i = 0; i < TPW; i++) {
-            const int sb = wave * (TPW / 4) + (i >> 2), h = (i >> 1) & 1, l0 = (i & 1) * 16;
-            // row n's block sb; the lane's code bytes start 4kg bytes into
-            // each field.  Staged bytes keep their offset mod 4, so a field
-            // at an offset of 2 mod 4 is read as two dwords and realigned.
-            const uint32_t blk = rowoff + 210u * (uint32_t)sb;
-            const uint32_t qoff = blk + 4u * (uint32_t)kg;
-            const uint32_t *q = stage + (qoff >> 2);
-            const uint32_t sel = (qoff & 2u) ? 0x05040302u : 0x03020100u;
-            const int fa = (64 * ((i >> 1) & 1) + (i & 1) * 16) / 4;  // ql, groups 0 and 2
-            const int fb = fa + 8;                                           // ql, groups 1 and 3
-            const int fh = (128 + 32 * ((i >> 1) & 1) + (i & 1) * 16) / 4;  // qh
-            const uint32_t qa = __builtin_amdgcn_perm(q[fa + 1], q[fa], sel);
-            const uint32_t qb = __builtin_amdgcn_perm(q[fb + 1], q[fb], sel);
-            const uint32_t hx = __builtin_amdgcn_perm(q[fh + 1], q[fh], sel) ^ 0xAAAAAAAAu;
-            // codes 4(q - 32) as signed bytes: low four bits to bits 2..5,
-            // the two top bits to bits 6..7 with the upper one flipped
-            v4i B;
-            B[0] = (int)(((qa << 2) & 0x3C3C3C3Cu) | ((hx << 6) & 0xC0C0C0C0u));
-            B[1] = (int)(((qb << 2) & 0x3C3C3C3Cu) | ((hx << 4) & 0xC0C0C0C0u));
-            B[2] = (int)(((qa >> 2) & 0x3C3C3C3Cu) | ((hx << 2) & 0xC0C0C0C0u));
-            B[3] = (int)(((qb >> 2) & 0x3C3C3C3Cu) | (hx & 0xC0C0C0C0u));
-            const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[i], B, zero, 0, 0, 0);
-            // row n, group kg: d / 4 (the codes carry a factor 4) and the
-            // sub-block scale sc[8h + 2kg + l0 / 16]
-            const float sc = (float)st8[blk + 2u * (uint32_t)kg + (uint32_t)(192 + 8 * h + l0 / 16)];
-            const float d = (float)*reinterpret_cast<const _Float16 *>(st8 + blk + 208u);
-            acc = fmaf(d * 0.25f * sc * fr[i], digits_sum(D[0], D[1], D[2]), acc);
+            if (i + 1 < TPW) fetch<TPW>(stage, rowoff, wave, kg, i + 1, fd[i + 1]);
+            const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[i], codes(fd[i]), zero, 0, 0, 0);
+            if (i > 0) acc = fmaf(fd[i - 1].ds * fr[i - 1], digits_sum(Dp[0], Dp[1], Dp[2]), acc);
+            Dp = D;
         }
+        acc = fmaf(fd[TPW - 1].ds * fr[TPW - 1], digits_sum(Dp[0], Dp[1], Dp[2]), acc);
         // the four groups of row n (lanes n, n + 16, n + 32, n + 48), then
         // the waves in order
         acc += __shfl_xor(acc, 16);
