@@ -475,5 +475,213 @@ __global__ void __launch_bounds__(512) qgemm_kernel(GemmParams p) {
     }
 }
 
+// ------------------------------------------------ batch 1..8: packed parts
+//
+// At most 8 batch rows.  The hi and lo parts share one A operand: row b
+// holds hi of batch row b and row 8 + b its lo, so one instruction per
+// block does the work of the two above, and lane (r, q + 2) ends with the
+// lo parts' sums of the batch rows whose hi parts' sums lane (r, q) holds.
+//
+// The activations are the kernel's largest stream (a 16-row tile re-reads
+// its batch rows' activations, 8 KB per chunk at batch 8, for ~2.3-2.8 KB
+// of weights), and each chunk waits for them: with no activation loads at
+// all the batch-8 Q5_K 14336 x 4096 GEMV took 15.7 us instead of 27.6 us.
+// So both streams run two chunks ahead here.  Lane (r, q) loads four of
+// the eight columns of its block (r < 8 the first four of batch row r,
+// r >= 8 the last four of batch row r - 8: 16 bytes per lane and block),
+// splits them into hi and lo parts and trades the half its partner needs
+// (lane r +- 8, the same row of 16 lanes) with one DPP rotation.  The
+// weights of a chunk are staged into the wave's LDS slot at the start of
+// the chunk, and that register buffer is refilled at once with the chunk
+// two ahead.
+template <class F, bool RA, int UNITS>
+__global__ void __launch_bounds__(512) qgemm8_kernel(GemmParams p) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int r = lane & 15, q = lane >> 4;
+    const int tpw = kWaves / p.ks;
+    const int64_t tile = (int64_t)blockIdx.x * tpw + wave / p.ks;
+    const int ksi = wave % p.ks;
+    const int c0 = (int)((int64_t)ksi * p.nchunks / p.ks);
+    const int c1 = (int)((int64_t)(ksi + 1) * p.nchunks / p.ks);
+    uint8_t *stage = smem + wave * kTileRows * p.slot;
+    float *red = (float *)(smem + kWaves * kTileRows * p.slot);
+
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (tile < p.tiles && c0 < c1) {
+        const uint64_t tb = (uint64_t)tile * kTileRows * p.row_bytes;
+        const uint8_t *gp = p.W + tb;
+        const uint8_t *al = (const uint8_t *)((uintptr_t)gp & ~(uintptr_t)15);
+        const uint32_t d0 = (uint32_t)(gp - al);
+        const uint64_t rem = (p.w_bytes - tb + d0 + 15) & ~(uint64_t)15;
+        const rsrc_t rw = make_rsrc(al, rem > 0xFFFFFFF0ull ? 0xFFFFFFF0u : (uint32_t)rem);
+        const int nunits = kTileRows * p.nu;
+        uint32_t u_row[UNITS], u_off[UNITS];
+#pragma unroll
+        for (int j = 0; j < UNITS; j++) {
+            const int u = lane + 64 * j, uu = u < nunits ? u : 0;
+            const int rr = uu / p.nu;
+            u_row[j] = (uint32_t)rr;
+            u_off[j] = 16u * (uint32_t)(uu - rr * p.nu);
+        }
+        auto w_issue = [&](int c, u32x4 (&w)[UNITS]) {
+#pragma unroll
+            for (int j = 0; j < UNITS; j++) {
+                if (lane + 64 * j < nunits) {
+                    const uint32_t base =
+                        (d0 + u_row[j] * p.row_bytes + (uint32_t)c * F::CHUNK) & ~15u;
+                    w[j] = __builtin_bit_cast(
+                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, base + u_off[j], 0,
+                                                                     kStream));
+                }
+            }
+        };
+        auto w_store = [&](const u32x4 (&w)[UNITS]) {
+#pragma unroll
+            for (int j = 0; j < UNITS; j++)
+                if (lane + 64 * j < nunits)
+                    *(u32x4 *)(stage + u_row[j] * p.slot + u_off[j]) = w[j];
+        };
+        const rsrc_t rx = make_rsrc(p.X, 4u * p.cols * (uint32_t)p.batch);
+        const int b = r & 7, hh = r >> 3;
+        // (plain arrays: this compiler mis-evaluated the element-wise bf16
+        // split when the four values were taken from a vector type by a
+        // loop index, using the first value for the second)
+        auto x_issue = [&](int c, uint32_t (&x)[8][4]) {
+#pragma unroll
+            for (int kb = 0; kb < 8; kb++) {
+                const uint32_t col = (uint32_t)c * kChunk + 32u * kb + 8u * q + 4u * hh;
+                const uint32_t off = (b < p.batch && col < p.cols)
+                                         ? 4u * ((uint32_t)b * p.cols + col) : 0x80000000u;
+                const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+                x[kb][0] = v[0];
+                x[kb][1] = v[1];
+                x[kb][2] = v[2];
+                x[kb][3] = v[3];
+            }
+        };
+        // the operand of lane (r, q) for one block from its four values
+        auto xop = [&](const uint32_t (&v)[4]) {
+            uint32_t h[2], l[2];
+#pragma unroll
+            for (int i = 0; i < 2; i++) {
+                const float x0 = __builtin_bit_cast(float, v[2 * i]);
+                const float x1 = __builtin_bit_cast(float, v[2 * i + 1]);
+                const bf16x2 hv = {(__bf16)x0, (__bf16)x1};
+                h[i] = __builtin_bit_cast(uint32_t, hv);
+                const float h0 = __builtin_bit_cast(float, h[i] << 16);
+                const float h1 = __builtin_bit_cast(float, h[i] & 0xFFFF0000u);
+                const bf16x2 lv = {(__bf16)(x0 - h0), (__bf16)(x1 - h1)};
+                l[i] = __builtin_bit_cast(uint32_t, lv);
+            }
+            // r < 8 keeps its hi parts and takes the partner's hi parts of
+            // the last four columns; r >= 8 keeps its lo parts and takes the
+            // partner's lo parts of the first four
+            const uint32_t t0 = dpp_u<0x128>(hh ? h[0] : l[0]);  // row_ror:8
+            const uint32_t t1 = dpp_u<0x128>(hh ? h[1] : l[1]);
+            u32x4 a;
+            a[0] = hh ? t0 : h[0];
+            a[1] = hh ? t1 : h[1];
+            a[2] = hh ? l[0] : t0;
+            a[3] = hh ? l[1] : t1;
+            return a;
+        };
+        const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};
+        const uint32_t keep_lo = q < 2 ? 0xFFFFFFFFu : 0u;  // Q6_K: lanes of the first group
+
+        auto chunk = [&](int c, uint32_t (&xc)[8][4], u32x4 (&wc)[UNITS], auto guard_tag) {
+            constexpr bool GUARD = decltype(guard_tag)::value;
+            const int nkb = GUARD && c == p.nchunks - 1 ? p.last_nkb : 8;
+            // chunk c's weights into the slot (the previous chunk's reads of
+            // it are done: a wave's LDS accesses are in order), then the
+            // buffer takes chunk c + 2
+            w_store(wc);
+            if (c + 2 < c1) w_issue(c + 2, wc);
+            u32x4 a[8];
+#pragma unroll
+            for (int kb = 0; kb < 8; kb++) a[kb] = xop(xc[kb]);
+            if (c + 2 < c1) x_issue(c + 2, xc);
+            const uint32_t delta = (d0 + (uint32_t)r * p.row_bytes + (uint32_t)c * F::CHUNK) & 15u;
+            const mx::RowRd<RA> rd = mx::make_rowrd<RA>(stage + r * p.slot, delta, 0);
+            const typename F::Head hd = F::template head<RA>(rd, q);
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kb = 0; kb < 8; kb++) {
+                if (!GUARD || kb < nkb) {
+                    const Blk bk = F::template block<RA>(rd, hd, kb, q);
+                    if constexpr (F::TWO) {
+                        u32x4 ca, cb;
+#pragma unroll
+                        for (int i = 0; i < 4; i++) {
+                            ca[i] = bk.c[i] & keep_lo;
+                            cb[i] = bk.c[i] & ~keep_lo;
+                        }
+                        const f32x4 da = mfma(a[kb], ca, z);
+                        const f32x4 db = mfma(a[kb], cb, z);
+#pragma unroll
+                        for (int i = 0; i < 4; i++)
+                            acc[i] = fmaf(bk.s2, db[i], fmaf(bk.s, da[i], acc[i]));
+                    } else {
+                        const f32x4 d = mfma(a[kb], bk.c, z);
+#pragma unroll
+                        for (int i = 0; i < 4; i++) acc[i] = fmaf(bk.s, d[i], acc[i]);
+                        if constexpr (F::MINS) {
+                            const f32x4 sm = mfma(a[kb], ones, z);
+#pragma unroll
+                            for (int i = 0; i < 4; i++) acc[i] = fmaf(-bk.dm, sm[i], acc[i]);
+                        }
+                    }
+                }
+            }
+        };
+        uint32_t xA[8][4], xB[8][4];
+        u32x4 wA[UNITS], wB[UNITS];
+        x_issue(c0, xA);
+        w_issue(c0, wA);
+        if (c0 + 1 < c1) {
+            x_issue(c0 + 1, xB);
+            w_issue(c0 + 1, wB);
+        }
+        // chunks in pairs (buffers A, B) while neither is the wave's last;
+        // the last chunk checks the row's block count
+        int c = c0;
+        for (; c + 2 < c1; c += 2) {
+            chunk(c, xA, wA, std::false_type{});
+            chunk(c + 1, xB, wB, std::false_type{});
+        }
+        if (c + 1 == c1) {
+            chunk(c, xA, wA, std::true_type{});
+        } else {
+            chunk(c, xA, wA, std::false_type{});
+            chunk(c + 1, xB, wB, std::true_type{});
+        }
+    }
+    // lane (r, q + 2) holds the lo parts' sums of the batch rows whose hi
+    // parts' sums lane (r, q) holds
+#pragma unroll
+    for (int i = 0; i < 4; i++) acc[i] += __shfl_xor(acc[i], 32);
+
+    // partial sums of the ks waves of a tile, added in wave order
+    const int64_t row = tile * kTileRows + r;
+    if (p.ks > 1) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) red[(wave * 4 + i) * 64 + lane] = acc[i];
+        __syncthreads();
+        if (ksi == 0 && tile < p.tiles) {
+            for (int w = 1; w < p.ks; w++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) acc[i] += red[((wave + w) * 4 + i) * 64 + lane];
+        }
+    }
+    if (ksi == 0 && tile < p.tiles && row < p.rows && q < 2) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int bo = 4 * q + i;
+            if (bo < p.batch) p.Y[(int64_t)bo * p.rows + row] = acc[i];
+        }
+    }
+}
+
 }  // namespace gm
 }  // namespace qg

@@ -9,6 +9,11 @@
 #ifndef QG_GEMM_KS
 #define QG_GEMM_KS 0
 #endif
+// 1: at most 8 batch rows run on gm::qgemm8_kernel (packed hi and lo parts,
+// both streams two chunks ahead).
+#ifndef QG_GEMM8
+#define QG_GEMM8 1
+#endif
 
 namespace qg {
 namespace host {
@@ -21,6 +26,16 @@ constexpr int gemm_units(int chunk) { return (16 * gemm_nu(chunk) + 63) / 64; }
 template <class F, int NB, bool RA>
 int launch_gemm_t(const gm::GemmParams &p, int grid, size_t lds, hipStream_t st) {
     constexpr int U = gemm_units(F::CHUNK);
+    if constexpr (NB == 1) {
+        if (QG_GEMM8 && p.batch <= 8) {
+            hipLaunchKernelGGL((gm::qgemm8_kernel<F, RA, U>), dim3(grid), dim3(64 * gm::kWaves),
+                               lds, st, p);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return fail(QG_ELAUNCH, "qgemv: launch failed: %s", hipGetErrorString(e));
+            return QG_OK;
+        }
+    }
     hipLaunchKernelGGL((gm::qgemm_kernel<F, NB, RA, U>), dim3(grid), dim3(64 * gm::kWaves), lds,
                        st, p);
     const hipError_t e = hipGetLastError();
