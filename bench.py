@@ -129,7 +129,7 @@ def measured_traffic():
 class Gemv:
     """A GEMV workload with enough device copies of W to stay cold."""
 
-    def __init__(self, case, batch, torch, q, q8act=False):
+    def __init__(self, case, batch, torch, q, q8act=False, ws=False):
         import synth
         self.case, self.batch, self.q, self.torch = case, batch, q, torch
         W, X = synth.gemv_inputs(case, batch)
@@ -141,12 +141,21 @@ class Gemv:
         self.Y = torch.empty(batch, case.rows, device="cuda")
         self.i = 0
         self.q8act = q8act
+        # qgemv_ws: the caller-provided workspace, allocated once
+        self.ws = None
+        if ws:
+            need = q.qgemv_ws_bytes(case.fmt, case.rows, case.cols, batch)
+            self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        self.use_ws = ws
 
     def launch(self):
         W = self.copies[self.i % len(self.copies)]
         self.i += 1
         if self.q8act:
             self.q.qgemv_q8act(self.case.fmt, W, self.case.rows, self.case.cols, self.X, self.Y)
+        elif self.use_ws:
+            self.q.qgemv_ws(self.case.fmt, W, self.case.rows, self.case.cols, self.X, self.Y,
+                            self.batch, self.ws)
         else:
             self.q.qgemv(self.case.fmt, W, self.case.rows, self.case.cols, self.X, self.Y,
                          self.batch)
@@ -461,6 +470,8 @@ ARITH = {
                    "run's max) on the matrix cores, exact int32 sums, f32 per run",
     "mfma_f16": "f16 codes x f16 hi + lo activation parts on the matrix cores, f32 sums",
     "mfma_bf16": "bf16 codes x bf16 hi + lo activation parts on the matrix cores, f32 sums",
+    "mfma_bf16_ws": "bf16 codes x bf16 hi + lo activation parts on the matrix cores, f32 sums, "
+                    "column ranges added in a second kernel",
     "q8act": "int8 codes x int8 activations (per 16 columns), exact int32 sums, f32 per group",
     "moe": "f64 router, f32 expert GEMVs on the vector ALUs",
     "moe_q8": "f64 router, expert GEMVs as int8 codes x int8 activations (per 16 columns), "
@@ -473,7 +484,7 @@ def gemv_arith(q):
     """The arithmetic the library reports for its last GEMV call."""
     return ARITH[{"valu_f32": "valu_f32", "valu_q6k_int": "valu_q6k_int",
                   "mfma_i8_q6k": "mfma_i8_q6k", "mx_f16": "mfma_f16", "gemm_bf16": "mfma_bf16",
-                  "valu_q8act": "q8act"}[q.qg_last_kernel()]]
+                  "gemm_ws_bf16": "mfma_bf16_ws", "valu_q8act": "q8act"}[q.qg_last_kernel()]]
 
 
 def main():
@@ -508,19 +519,25 @@ def main():
         del head
 
     if not args.quick:
-        sweep = [("q8_0_256x1024", 1, False), ("q6_k_151936x2048", 1, False)]
-        sweep += [("q5_k_14336x4096", b, False) for b in (1, 4, 8)]
-        sweep += [("q4_0_4096x14336", b, False) for b in (1, 4, 8)]
+        # (workload, batch, variant): "" qgemv, "q8act" qgemv_q8act, "ws" qgemv_ws
+        sweep = [("q8_0_256x1024", 1, ""), ("q6_k_151936x2048", 1, "")]
+        sweep += [("q5_k_14336x4096", b, "") for b in (1, 4, 8)]
+        sweep += [("q4_0_4096x14336", b, "") for b in (1, 4, 8)]
         # prefill-sized batches
-        sweep += [("q4_k_4096x4096", b, False) for b in (16, 32, 64)]
+        sweep += [("q4_k_4096x4096", b, "") for b in (16, 32, 64)]
+        # the batched shapes again through qgemv_ws (activations shared
+        # through LDS, a workspace)
+        sweep += [("q5_k_14336x4096", b, "ws") for b in (4, 8)]
+        sweep += [("q4_0_4096x14336", b, "ws") for b in (4, 8)]
+        sweep += [("q4_k_4096x4096", b, "ws") for b in (16, 32, 64)]
         # the int8-activation variant (batch 1)
-        sweep += [("q4_k_4096x4096", 1, True), ("q6_k_151936x2048", 1, True)]
-        for name, b, q8 in sweep:
-            key = f"{name}_b{b}" + ("_q8act" if q8 else "")
+        sweep += [("q4_k_4096x4096", 1, "q8act"), ("q6_k_151936x2048", 1, "q8act")]
+        for name, b, var in sweep:
+            key = f"{name}_b{b}" + (f"_{var}" if var else "")
             if only and key not in only:
                 continue
             case = synth.GEMV_CASES[name]
-            w = Gemv(case, b, torch, q, q8act=q8)
+            w = Gemv(case, b, torch, q, q8act=var == "q8act", ws=var == "ws")
             steps = max(50, min(args.steps, int(4e9 // w.wbytes)))
             wall, ev_ms = time_launches(torch, w, steps, args.warmup, args.warm_seconds, scrub)
             per_us = ev_ms * 1e3 / steps

@@ -34,6 +34,8 @@ SIGNATURES = {
     "qg_last_error": ([], ctypes.c_char_p),
     "qg_last_kernel": ([], ctypes.c_char_p),
     "qgemv": ([_INT, _P, _I64, _I64, _P, _P, _INT, _P], _INT),
+    "qgemv_ws": ([_INT, _P, _I64, _I64, _P, _P, _INT, _P, ctypes.c_size_t, _P], _INT),
+    "qgemv_ws_bytes": ([_INT, _I64, _I64, _INT], ctypes.c_size_t),
     "qgemv_q8act": ([_INT, _P, _I64, _I64, _P, _P, _P], _INT),
     "moe_ffn_workspace_bytes": ([_I64, _I64, _I64], ctypes.c_size_t),
     "moe_ffn": ([_P, _P, _P, _P, _INT, _P, _INT, _P, _INT, _P, _I64, _I64, _I64, _I64,
@@ -123,7 +125,7 @@ def qg_last_error() -> str:
 
 
 def qg_last_kernel() -> str:
-    """The arithmetic of the last successful qgemv / qgemv_q8act on this thread."""
+    """The arithmetic of the last successful qgemv / qgemv_ws / qgemv_q8act on this thread."""
     return load_library().qg_last_kernel().decode()
 
 
@@ -227,6 +229,20 @@ def moe_ffn_tokens(x, residual, y, router, gate_fmt: int, gate, up_fmt: int, up,
                                        _ptr(sel_weights), _ptr(workspace), workspace_bytes,
                                        _stream(stream))
     _check(rc, "moe_ffn_tokens")
+
+
+def qgemv_ws_bytes(fmt: int, rows: int, cols: int, batch: int) -> int:
+    return load_library().qgemv_ws_bytes(fmt, rows, cols, batch)
+
+
+def qgemv_ws(fmt: int, W, rows: int, cols: int, X, Y, batch: int, workspace=None,
+             workspace_bytes: Optional[int] = None, stream=None) -> None:
+    """qgemv with a caller-provided workspace for batch >= 2 (see include/qgemv.h)."""
+    if workspace_bytes is None:
+        workspace_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = load_library().qgemv_ws(fmt, _ptr(W), rows, cols, _ptr(X), _ptr(Y), batch,
+                                 _ptr(workspace), workspace_bytes, _stream(stream))
+    _check(rc, "qgemv_ws")
 
 
 def qgemv_q8act(fmt: int, W, rows: int, cols: int, X, Y, stream=None) -> None:

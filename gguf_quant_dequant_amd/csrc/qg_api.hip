@@ -250,27 +250,34 @@ const char *qg_last_kernel(void) { return g_kernel; }
 // rows; F32 above 8 as groups of 8 (see qgemv).
 constexpr int kMaxBatch = 64;
 
-int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
-          int batch, void *stream) {
+// The argument checks qgemv and qgemv_ws share.
+static int check_gemv(const char *who, int fmt, const void *W, int64_t rows, int64_t cols,
+                      const float *X, const float *Y, int batch) {
     const Geom g = geom(fmt);
-    if (g.elems == 0) return fail(QG_EUNSUPPORTED, "qgemv: unknown format %d", fmt);
-    if (!W || !X || !Y) return fail(QG_EINVAL, "qgemv: W, X and Y must be non-NULL");
+    if (g.elems == 0) return fail(QG_EUNSUPPORTED, "%s: unknown format %d", who, fmt);
+    if (!W || !X || !Y) return fail(QG_EINVAL, "%s: W, X and Y must be non-NULL", who);
     if (rows <= 0 || cols <= 0)
-        return fail(QG_EINVAL, "qgemv: rows (%lld) and cols (%lld) must be positive",
+        return fail(QG_EINVAL, "%s: rows (%lld) and cols (%lld) must be positive", who,
                     (long long)rows, (long long)cols);
     if (cols % g.elems != 0)
-        return fail(QG_EUNSUPPORTED, "qgemv: %s needs cols to be a multiple of %d (got %lld)",
+        return fail(QG_EUNSUPPORTED, "%s: %s needs cols to be a multiple of %d (got %lld)", who,
                     fmt_name(fmt), g.elems, (long long)cols);
     if (batch < 1 || batch > kMaxBatch)
-        return fail(QG_EUNSUPPORTED, "qgemv: batch %d outside 1..%d", batch, kMaxBatch);
+        return fail(QG_EUNSUPPORTED, "%s: batch %d outside 1..%d", who, batch, kMaxBatch);
     if (!aligned_to(W, fmt == QG_F32 ? 4 : 2))
-        return fail(QG_EINVAL, "qgemv: W is not %d-byte aligned", fmt == QG_F32 ? 4 : 2);
+        return fail(QG_EINVAL, "%s: W is not %d-byte aligned", who, fmt == QG_F32 ? 4 : 2);
     if (!aligned_to(X, 4) || !aligned_to(Y, 4))
-        return fail(QG_EINVAL, "qgemv: X and Y must be 4-byte aligned");
-    if (rows >= ((int64_t)1 << 31)) return fail(QG_EUNSUPPORTED, "qgemv: rows must be < 2^31");
-    if (cols > 65536) return fail(QG_EUNSUPPORTED, "qgemv: cols must be <= 65536");
+        return fail(QG_EINVAL, "%s: X and Y must be 4-byte aligned", who);
+    if (rows >= ((int64_t)1 << 31)) return fail(QG_EUNSUPPORTED, "%s: rows must be < 2^31", who);
+    if (cols > 65536) return fail(QG_EUNSUPPORTED, "%s: cols must be <= 65536", who);
     if (fmt == QG_F32 && cols % 4 != 0)
-        return fail(QG_EUNSUPPORTED, "qgemv: F32 rows must be a multiple of 4 floats");
+        return fail(QG_EUNSUPPORTED, "%s: F32 rows must be a multiple of 4 floats", who);
+    return QG_OK;
+}
+
+int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
+          int batch, void *stream) {
+    if (const int rcv = check_gemv("qgemv", fmt, W, rows, cols, X, Y, batch)) return rcv;
     const int64_t rb = qg_row_bytes(fmt, cols);
     hipStream_t st = (hipStream_t)stream;
     if (const int rc0 = no_pending_error("qgemv")) return rc0;
@@ -346,6 +353,43 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
         if (rc != QG_OK) return rc;
     }
     g_kernel = (fmt == QG_Q6_K && batch == 1) ? "valu_q6k_int" : "valu_f32";
+    return ok();
+}
+
+size_t qgemv_ws_bytes(int fmt, int64_t rows, int64_t cols, int batch) {
+    const Geom g = geom(fmt);
+    if (g.elems == 0 || fmt == QG_F32 || rows <= 0 || cols <= 0 || cols % g.elems != 0 ||
+        batch < 2 || batch > kMaxBatch || rows >= ((int64_t)1 << 31) || cols > 65536)
+        return 0;
+    const int kg = ws_kg(rows, cols);
+    if (kg == 1) return 0;
+    const int nb = batch < 32 ? batch : 32;
+    return (size_t)kg * (size_t)nb * (size_t)rows * sizeof(float);
+}
+
+int qgemv_ws(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
+             int batch, void *workspace, size_t workspace_bytes, void *stream) {
+    if (const int rcv = check_gemv("qgemv_ws", fmt, W, rows, cols, X, Y, batch)) return rcv;
+    // no batched matrix-core work: qgemv's kernels, no workspace
+    if (fmt == QG_F32 || batch == 1) return qgemv(fmt, W, rows, cols, X, Y, batch, stream);
+    const size_t need = qgemv_ws_bytes(fmt, rows, cols, batch);
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(QG_EINVAL, "qgemv_ws: the workspace holds %zu bytes; this call needs %zu "
+                               "(qgemv_ws_bytes)", workspace ? workspace_bytes : (size_t)0, need);
+    if (need > 0 && !aligned_to(workspace, 16))
+        return fail(QG_EINVAL, "qgemv_ws: the workspace must be 16-byte aligned");
+    const int64_t rb = qg_row_bytes(fmt, cols);
+    hipStream_t st = (hipStream_t)stream;
+    if (const int rc0 = no_pending_error("qgemv_ws")) return rc0;
+    // launches of up to 32 batch rows, each reading the weights once; they
+    // run one after another on the stream and reuse the workspace
+    for (int b0 = 0; b0 < batch; b0 += 32) {
+        const int nb = batch - b0 < 32 ? batch - b0 : 32;
+        const int rc = gemm_ws(fmt, W, rows, cols, X + (int64_t)b0 * cols,
+                               Y + (int64_t)b0 * rows, nb, rb, (float *)workspace, st);
+        if (rc != QG_OK) return rc;
+    }
+    g_kernel = "gemm_ws_bf16";
     return ok();
 }
 

@@ -321,16 +321,17 @@ __global__ void __launch_bounds__(512) qgemm_kernel(GemmParams p) {
             u_off[j] = 16u * (uint32_t)(uu - rr * p.nu);
         }
         u32x4 wreg[UNITS];
+        // branch-free: a unit past the tile's segments reads an out-of-range
+        // offset (zeros, no memory access); loads under a branch were each
+        // followed by a wait for all loads
         auto w_issue = [&](int c) {
 #pragma unroll
             for (int j = 0; j < UNITS; j++) {
-                if (lane + 64 * j < nunits) {
-                    const uint32_t base =
-                        (d0 + u_row[j] * p.row_bytes + (uint32_t)c * F::CHUNK) & ~15u;
-                    wreg[j] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, base + u_off[j], 0,
-                                                                     kStream));
-                }
+                const uint32_t base =
+                    (d0 + u_row[j] * p.row_bytes + (uint32_t)c * F::CHUNK) & ~15u;
+                const uint32_t off = lane + 64 * j < nunits ? base + u_off[j] : 0xFFFFFFF0u;
+                wreg[j] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStream));
             }
         };
         // the chunk's rows into the wave's LDS slot (the previous chunk's
@@ -525,16 +526,21 @@ __global__ void __launch_bounds__(512) qgemm8_kernel(GemmParams p) {
             u_row[j] = (uint32_t)rr;
             u_off[j] = 16u * (uint32_t)(uu - rr * p.nu);
         }
-        auto w_issue = [&](int c, u32x4 (&w)[UNITS]) {
+        // Every chunk issues the same loads, and none sits under a branch:
+        // a unit past the tile's segments, or a chunk past the wave's range
+        // (valid false), reads zeros from an out-of-range offset.  Loads
+        // under a branch, or a count that differs between paths, made the
+        // compiler wait for all loads, and the chunks ahead were no longer in
+        // flight.
+        auto w_issue = [&](int c, u32x4 (&w)[UNITS], bool valid) {
 #pragma unroll
             for (int j = 0; j < UNITS; j++) {
-                if (lane + 64 * j < nunits) {
-                    const uint32_t base =
-                        (d0 + u_row[j] * p.row_bytes + (uint32_t)c * F::CHUNK) & ~15u;
-                    w[j] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, base + u_off[j], 0,
-                                                                     kStream));
-                }
+                const uint32_t base =
+                    (d0 + u_row[j] * p.row_bytes + (uint32_t)c * F::CHUNK) & ~15u;
+                const uint32_t off =
+                    valid && lane + 64 * j < nunits ? base + u_off[j] : 0xFFFFFFF0u;
+                w[j] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStream));
             }
         };
         auto w_store = [&](const u32x4 (&w)[UNITS]) {
@@ -548,11 +554,11 @@ __global__ void __launch_bounds__(512) qgemm8_kernel(GemmParams p) {
         // (plain arrays: this compiler mis-evaluated the element-wise bf16
         // split when the four values were taken from a vector type by a
         // loop index, using the first value for the second)
-        auto x_issue = [&](int c, uint32_t (&x)[8][4]) {
+        auto x_issue = [&](int c, uint32_t (&x)[8][4], bool valid) {
 #pragma unroll
             for (int kb = 0; kb < 8; kb++) {
                 const uint32_t col = (uint32_t)c * kChunk + 32u * kb + 8u * q + 4u * hh;
-                const uint32_t off = (b < p.batch && col < p.cols)
+                const uint32_t off = (valid && b < p.batch && col < p.cols)
                                          ? 4u * ((uint32_t)b * p.cols + col) : 0x80000000u;
                 const auto v = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
                 x[kb][0] = v[0];
@@ -597,11 +603,11 @@ __global__ void __launch_bounds__(512) qgemm8_kernel(GemmParams p) {
             // it are done: a wave's LDS accesses are in order), then the
             // buffer takes chunk c + 2
             w_store(wc);
-            if (c + 2 < c1) w_issue(c + 2, wc);
+            w_issue(c + 2, wc, c + 2 < c1);
             u32x4 a[8];
 #pragma unroll
             for (int kb = 0; kb < 8; kb++) a[kb] = xop(xc[kb]);
-            if (c + 2 < c1) x_issue(c + 2, xc);
+            x_issue(c + 2, xc, c + 2 < c1);
             const uint32_t delta = (d0 + (uint32_t)r * p.row_bytes + (uint32_t)c * F::CHUNK) & 15u;
             const mx::RowRd<RA> rd = mx::make_rowrd<RA>(stage + r * p.slot, delta, 0);
             const typename F::Head hd = F::template head<RA>(rd, q);
@@ -637,12 +643,10 @@ __global__ void __launch_bounds__(512) qgemm8_kernel(GemmParams p) {
         };
         uint32_t xA[8][4], xB[8][4];
         u32x4 wA[UNITS], wB[UNITS];
-        x_issue(c0, xA);
-        w_issue(c0, wA);
-        if (c0 + 1 < c1) {
-            x_issue(c0 + 1, xB);
-            w_issue(c0 + 1, wB);
-        }
+        x_issue(c0, xA, true);
+        w_issue(c0, wA, true);
+        x_issue(c0 + 1, xB, c0 + 1 < c1);
+        w_issue(c0 + 1, wB, c0 + 1 < c1);
         // chunks in pairs (buffers A, B) while neither is the wave's last;
         // the last chunk checks the row's block count
         int c = c0;

@@ -287,6 +287,9 @@ int dispatch_down(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_gateup_q8(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_down_q8(int fmt, const MoeParams &p, hipStream_t st);
 int try_q6mx(const GemvParams &p, hipStream_t st, bool *done);
+int ws_kg(int64_t rows, int64_t cols);
+int gemm_ws(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
+            int batch, int64_t rb, float *part, hipStream_t st);
 
 }  // namespace host
 }  // namespace qg

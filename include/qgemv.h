@@ -14,6 +14,8 @@
  *            that feeds its router.
  *   moe_ffn_tokens  the same FFN for up to 8 decode tokens at once, each
  *            routed on its own, the expert GEMVs grouped by expert.
+ *   qgemv_ws  qgemv at batch >= 2 with a caller-provided workspace (the
+ *            activations shared through LDS; qgemv_ws_bytes sizes it).
  *   qgemv_q8act  qgemv at batch 1 on int8-quantised activations (integer
  *            dot products; the pages' lossy fast variant).
  *   moe_ffn_q8act  moe_ffn with its expert GEMVs on int8-quantised
@@ -107,7 +109,7 @@ int64_t qg_row_bytes(int fmt, int64_t cols);
  * call on the same thread. */
 const char *qg_last_error(void);
 
-/* The arithmetic of the last qgemv or qgemv_q8act call on the calling
+/* The arithmetic of the last qgemv, qgemv_ws or qgemv_q8act call on the calling
  * thread that returned QG_OK ("" before any):
  *   "valu_f32"      f32 products and sums on the vector ALUs;
  *   "valu_q6k_int"  Q6_K at batch 1: integer activation digits, exact int32
@@ -116,6 +118,8 @@ const char *qg_last_error(void);
  *                   matrix cores (Q6_K batch-1 rows of up to 4096 columns);
  *   "mx_f16"        matrix cores, f16 codes x f16 hi + lo activation parts;
  *   "gemm_bf16"     matrix cores, bf16 codes x bf16 hi + lo activation parts;
+ *   "gemm_ws_bf16"  the same arithmetic, activation operands shared through
+ *                   LDS (qgemv_ws);
  *   "valu_q8act"    int8 codes x int8 activations (qgemv_q8act).
  * A static string; reporting only, no effect on any call. */
 const char *qg_last_kernel(void);
@@ -164,6 +168,39 @@ const char *qg_last_kernel(void);
  */
 int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
           float *Y, int batch, void *stream);
+
+/*
+ * qgemv_ws: qgemv with a caller-provided workspace, for batch >= 2.
+ *
+ * Same arguments, result and tolerance as qgemv (weight_matrix.rs
+ * apply_batch: each weight row's bytes read once per launch of up to 32
+ * batch rows and dotted with every activation of the batch), with the
+ * block formats at batch 2..64 on a kernel that loads each activation
+ * chunk once per workgroup of 8 row tiles and shares it through LDS.  A
+ * row's columns are split over several workgroups; their partial sums go
+ * to the workspace and a second kernel adds them per output in a fixed
+ * order, so results are deterministic run to run (they differ from
+ * qgemv's in rounding only).  F32 and batch 1 run qgemv itself.
+ *
+ *   workspace        device memory of at least qgemv_ws_bytes(fmt, rows,
+ *                    cols, batch) bytes, 16-byte aligned, owned by the
+ *                    caller; no initial contents needed.  May be NULL when
+ *                    that size is 0.  Calls that overlap in time on one
+ *                    workspace race.
+ *   workspace_bytes  its size.
+ *
+ * Errors as qgemv; QG_EINVAL for a missing, short or misaligned workspace.
+ * qg_last_kernel() reports "gemm_ws_bf16" for the batched kernel.
+ * Allocates nothing.
+ */
+int qgemv_ws(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
+             float *Y, int batch, void *workspace, size_t workspace_bytes,
+             void *stream);
+
+/* Workspace bytes qgemv_ws needs for these arguments: 0 when none is needed
+ * (F32, batch 1, a row split over a single workgroup) and for arguments
+ * qgemv_ws refuses.  Depends only on the arguments, not on the device. */
+size_t qgemv_ws_bytes(int fmt, int64_t rows, int64_t cols, int batch);
 
 /*
  * qgemv_q8act: the int8-activation variant of qgemv at batch 1 -- the
