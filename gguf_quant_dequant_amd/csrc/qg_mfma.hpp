@@ -140,56 +140,77 @@ __device__ void build_ximg(const float *__restrict__ X, uint32_t cols, uint32_t 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const rsrc_t rx = make_rsrc(X, xbytes);
-    for (int u = wave; u < nc * B; u += kWaves) {
-        const int c = u / B, b = u - c * B;
-        const uint32_t col = (uint32_t)c * kChunk + 4u * lane;
-        // columns past the row and batch rows past `batch` read as zero (an
-        // out-of-range offset reads zeros without a memory access)
-        const uint32_t xo =
-            (b < batch && col < cols) ? 4u * ((uint32_t)b * xstride + col) : 0xFFFFFFF0u;
-        const auto w = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
-        float v[4];
+    // the wave's units in rounds of XK: all loads of a round are issued
+    // before the first is converted (one load and its wait per unit left a
+    // memory latency per unit on the workgroup's start)
+    constexpr int XK = 8;
+    const int nu = nc * B;
+    for (int u0 = wave; u0 < nu; u0 += kWaves * XK) {
+        uint32_t wv[XK][4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) v[j] = __builtin_bit_cast(float, (uint32_t)w[j]);
-        float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
-        am = group_max<64>(am);
-        int e = 0;
-        if (am > 0.f && am <= 3.4028234663852886e38f) {
-            e = 14 - __builtin_amdgcn_frexp_expf(am);
-            e = e < -64 ? -64 : (e > 64 ? 64 : e);
+        for (int k = 0; k < XK; k++) {
+            const int u = u0 + k * kWaves;
+            const int c = u / B, b = u - c * B;
+            const uint32_t col = (uint32_t)c * kChunk + 4u * lane;
+            // units past the last, columns past the row and batch rows past
+            // `batch` read as zero (an out-of-range offset reads zeros
+            // without a memory access)
+            const uint32_t xo = (u < nu && b < batch && col < cols)
+                                    ? 4u * ((uint32_t)b * xstride + col) : 0xFFFFFFF0u;
+            const auto w = __builtin_amdgcn_raw_buffer_load_b128(rx, xo, 0, 0);
+            wv[k][0] = w[0];
+            wv[k][1] = w[1];
+            wv[k][2] = w[2];
+            wv[k][3] = w[3];
         }
-        float xs[4], r[4];
 #pragma unroll
-        for (int j = 0; j < 4; j++) xs[j] = __builtin_amdgcn_ldexpf(v[j], e);
-        const auto h01 = __builtin_amdgcn_cvt_pkrtz(xs[0], xs[1]);
-        const auto h23 = __builtin_amdgcn_cvt_pkrtz(xs[2], xs[3]);
-        r[0] = xs[0] - (float)h01[0];
-        r[1] = xs[1] - (float)h01[1];
-        r[2] = xs[2] - (float)h23[0];
-        r[3] = xs[3] - (float)h23[1];
-        const auto l01 = __builtin_amdgcn_cvt_pkrtz(r[0], r[1]);
-        const auto l23 = __builtin_amdgcn_cvt_pkrtz(r[2], r[3]);
-        uint8_t *rec = ximg + (size_t)c * REC;
-        const int g = lane >> 2, pos = 4 * (lane & 3);
-        u32x2 hv, lv;
-        hv[0] = __builtin_bit_cast(uint32_t, h01);
-        hv[1] = __builtin_bit_cast(uint32_t, h23);
-        lv[0] = __builtin_bit_cast(uint32_t, l01);
-        lv[1] = __builtin_bit_cast(uint32_t, l23);
-        *(u32x2 *)(rec + 2 * ((g * 2 * B + b) * 16 + pos)) = hv;
-        *(u32x2 *)(rec + 2 * ((g * 2 * B + B + b) * 16 + pos)) = lv;
-        if constexpr (SEEDS) {
-            float s = (xs[0] + xs[1]) + (xs[2] + xs[3]);
-            s = glanes == 8 ? group_sum<8>(s) : group_sum<4>(s);
-            if ((lane & (glanes - 1)) == 0) {
-                float *cp = (float *)(rec + ximg_a(B)) + (g * KH + b / 4) * 8;
-                cp[b & 3] = coff * s;
-                cp[4 + (b & 3)] = 0.f;
+        for (int k = 0; k < XK; k++) {
+            const int u = u0 + k * kWaves;
+            if (u >= nu) break;
+            const int c = u / B, b = u - c * B;
+            float v[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) v[j] = __builtin_bit_cast(float, wv[k][j]);
+            float am = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+            am = group_max<64>(am);
+            int e = 0;
+            if (am > 0.f && am <= 3.4028234663852886e38f) {
+                e = 14 - __builtin_amdgcn_frexp_expf(am);
+                e = e < -64 ? -64 : (e > 64 ? 64 : e);
             }
+            float xs[4], r[4];
+#pragma unroll
+            for (int j = 0; j < 4; j++) xs[j] = __builtin_amdgcn_ldexpf(v[j], e);
+            const auto h01 = __builtin_amdgcn_cvt_pkrtz(xs[0], xs[1]);
+            const auto h23 = __builtin_amdgcn_cvt_pkrtz(xs[2], xs[3]);
+            r[0] = xs[0] - (float)h01[0];
+            r[1] = xs[1] - (float)h01[1];
+            r[2] = xs[2] - (float)h23[0];
+            r[3] = xs[3] - (float)h23[1];
+            const auto l01 = __builtin_amdgcn_cvt_pkrtz(r[0], r[1]);
+            const auto l23 = __builtin_amdgcn_cvt_pkrtz(r[2], r[3]);
+            uint8_t *rec = ximg + (size_t)c * REC;
+            const int g = lane >> 2, pos = 4 * (lane & 3);
+            u32x2 hv, lv;
+            hv[0] = __builtin_bit_cast(uint32_t, h01);
+            hv[1] = __builtin_bit_cast(uint32_t, h23);
+            lv[0] = __builtin_bit_cast(uint32_t, l01);
+            lv[1] = __builtin_bit_cast(uint32_t, l23);
+            *(u32x2 *)(rec + 2 * ((g * 2 * B + b) * 16 + pos)) = hv;
+            *(u32x2 *)(rec + 2 * ((g * 2 * B + B + b) * 16 + pos)) = lv;
+            if constexpr (SEEDS) {
+                float s = (xs[0] + xs[1]) + (xs[2] + xs[3]);
+                s = glanes == 8 ? group_sum<8>(s) : group_sum<4>(s);
+                if ((lane & (glanes - 1)) == 0) {
+                    float *cp = (float *)(rec + ximg_a(B)) + (g * KH + b / 4) * 8;
+                    cp[b & 3] = coff * s;
+                    cp[4 + (b & 3)] = 0.f;
+                }
+            }
+            if (lane == 0)
+                ((float *)(rec + ximg_a(B) + ximg_c(B)))[4 * (b / 4) + (b & 3)] =
+                    __builtin_amdgcn_ldexpf(1.0f, 24 - e);
         }
-        if (lane == 0)
-            ((float *)(rec + ximg_a(B) + ximg_c(B)))[4 * (b / 4) + (b & 3)] =
-                __builtin_amdgcn_ldexpf(1.0f, 24 - e);
     }
 }
 
