@@ -87,6 +87,7 @@ __device__ __forceinline__ u32x4 codes_s8(uint32_t v0, uint32_t v1) {
     c[3] = pack2(sbyte<2>(v1), sbyte<3>(v1));
     return c;
 }
+
 __device__ __forceinline__ u32x4 codes_u8(uint32_t v0, uint32_t v1) {
     v0 = opaque(v0);
     v1 = opaque(v1);
@@ -95,6 +96,19 @@ __device__ __forceinline__ u32x4 codes_u8(uint32_t v0, uint32_t v1) {
     c[1] = pack2(ubyte<2>(v0), ubyte<3>(v0));
     c[2] = pack2(ubyte<0>(v1), ubyte<1>(v1));
     c[3] = pack2(ubyte<2>(v1), ubyte<3>(v1));
+    return c;
+}
+
+// Eight unsigned code bytes below 128 (two dwords) -> the eight bf16
+// values 128 + n: the byte n becomes the mantissa under the bf16 pattern of
+// 128 (0x4300), one byte permute per two codes.  The caller removes the 128
+// offset with the block's sum of activations.
+__device__ __forceinline__ u32x4 codes_u7_off128(uint32_t v0, uint32_t v1) {
+    u32x4 c;
+    c[0] = __builtin_amdgcn_perm(0x43434343u, v0, 0x04010400u);
+    c[1] = __builtin_amdgcn_perm(0x43434343u, v0, 0x04030402u);
+    c[2] = __builtin_amdgcn_perm(0x43434343u, v1, 0x04010400u);
+    c[3] = __builtin_amdgcn_perm(0x43434343u, v1, 0x04030402u);
     return c;
 }
 
@@ -115,11 +129,11 @@ struct Blk {
 // Q8_0: eight 34-byte blocks per chunk; f16 d at 0, int8 q at 2.
 struct GQ80 {
     static constexpr int CHUNK = 272;
-    static constexpr bool MINS = false, TWO = false;
+    static constexpr bool MINS = false, TWO = false, OFF128 = false;
     struct Head {};
     template <bool RA>
     __device__ static Head head(const mx::RowRd<RA> &, int) { return {}; }
-    template <bool RA>
+    template <bool RA, bool OFF>
     __device__ static Blk block(const mx::RowRd<RA> &rd, const Head &, int kb, int q) {
         Blk b;
         const int o = 34 * kb;
@@ -135,11 +149,11 @@ struct GQ80 {
 // Codes: nibble ^ 8 moved to the top of its byte, the signed 16 (q - 8).
 struct GQ40 {
     static constexpr int CHUNK = 144;
-    static constexpr bool MINS = false, TWO = false;
+    static constexpr bool MINS = false, TWO = false, OFF128 = false;
     struct Head {};
     template <bool RA>
     __device__ static Head head(const mx::RowRd<RA> &, int) { return {}; }
-    template <bool RA>
+    template <bool RA, bool OFF>
     __device__ static Blk block(const mx::RowRd<RA> &rd, const Head &, int kb, int q) {
         Blk b;
         const int o = 18 * kb;
@@ -157,10 +171,17 @@ struct GQ40 {
 // packed 6-bit (scale, min) at 4 (ferrox_q4_k_scale_min); Q4_K qs[128] at
 // 16, Q5_K qh[32] at 16 and qs[128] at 48.  Block g = 2p + u: nibble u of
 // qs[32p + l] (Q5_K: plus 16 * bit g of qh[l]); value d sc q - dmin m.
+// With OFF the codes enter as 128 + q (codes_u7_off128, four byte permutes
+// where the plain conversion takes twelve operations); the kernel then takes
+// the block's sum of (128 + q) x minus 128 times its sum of x before
+// scaling (off128), so a block of zero codes still gives exactly 0: the two
+// matrix-core sums differ by the factor 128 exactly.  That costs one fma per
+// output and block, which pays where one weight block meets few activation
+// rows.
 template <bool FIVE>
 struct GK45 {
     static constexpr int CHUNK = FIVE ? 176 : 144;
-    static constexpr bool MINS = true, TWO = false;
+    static constexpr bool MINS = true, TWO = false, OFF128 = true;
     static constexpr int QS = FIVE ? 48 : 16;
     struct Head {
         float d, dmin;
@@ -183,7 +204,7 @@ struct GK45 {
         }
         return h;
     }
-    template <bool RA>
+    template <bool RA, bool OFF>
     __device__ static Blk block(const mx::RowRd<RA> &rd, const Head &h, int g, int q) {
         Blk b;
         const int p = g >> 1, u = g & 1;
@@ -198,12 +219,14 @@ struct GK45 {
             mm = ((h.s2 >> (8 * j + 4)) & 15u) | (((h.s1 >> (8 * j)) >> 6) << 4);
         }
         const float sc = (float)(s & 63u), m = (float)(mm & 63u);
-        if constexpr (FIVE) {
-            const uint32_t n0 = u ? (a0 >> 4) & 0x0F0F0F0Fu : a0 & 0x0F0F0F0Fu;
-            const uint32_t n1 = u ? (a1 >> 4) & 0x0F0F0F0Fu : a1 & 0x0F0F0F0Fu;
-            const uint32_t b0 = ((h.h0 >> g) & 0x01010101u) << 4;
-            const uint32_t b1 = ((h.h1 >> g) & 0x01010101u) << 4;
-            b.c = codes_u8(n0 | b0, n1 | b1);
+        if constexpr (FIVE || OFF) {
+            uint32_t n0 = u ? (a0 >> 4) & 0x0F0F0F0Fu : a0 & 0x0F0F0F0Fu;
+            uint32_t n1 = u ? (a1 >> 4) & 0x0F0F0F0Fu : a1 & 0x0F0F0F0Fu;
+            if constexpr (FIVE) {
+                n0 |= ((h.h0 >> g) & 0x01010101u) << 4;
+                n1 |= ((h.h1 >> g) & 0x01010101u) << 4;
+            }
+            b.c = OFF ? codes_u7_off128(n0, n1) : codes_u8(n0, n1);
             b.s = h.d * sc;
         } else {
             const uint32_t mk = u ? 0xF0F0F0F0u : 0x0F0F0F0Fu;  // high nibbles in place: 16 q
@@ -223,7 +246,7 @@ struct GK45 {
 // two scale groups.  Codes are the signed bytes 4 (q - 32).
 struct GQ6K {
     static constexpr int CHUNK = 210;
-    static constexpr bool MINS = false, TWO = true;
+    static constexpr bool MINS = false, TWO = true, OFF128 = false;
     struct Head {
         float d4;
     };
@@ -231,7 +254,7 @@ struct GQ6K {
     __device__ static Head head(const mx::RowRd<RA> &rd, int) {
         return {f16_lo(rd.dw(208)) * 0.25f};
     }
-    template <bool RA>
+    template <bool RA, bool OFF>
     __device__ static Blk block(const mx::RowRd<RA> &rd, const Head &hd, int kb, int q) {
         Blk b;
         const int h = kb >> 2, t = kb & 3;
@@ -257,6 +280,15 @@ struct GQ6K {
 };
 
 // ---------------------------------------------------------------- kernel
+
+// A block's product sum with the codes' 128 offset removed (formats with
+// OFF128, blocks decoded with OFF): sum (128 + q) x - 128 sum x, exact for
+// zero codes.
+template <class F, bool OFF>
+__device__ __forceinline__ float off128(float d, float sm) {
+    if constexpr (F::OFF128 && OFF) return fmaf(-128.0f, sm, d);
+    return d;
+}
 
 template <int N>
 __device__ __forceinline__ void zero(f32x4 (&a)[N]) {
@@ -286,6 +318,13 @@ struct GemmParams {
 template <class F, int NB, bool RA, int UNITS>
 __global__ void __launch_bounds__(512) qgemm_kernel(GemmParams p) {
     constexpr int XK = 8 / NB, NS = 8 / XK;  // blocks per step, steps per chunk
+#ifndef QG_OFF_NB
+#define QG_OFF_NB 2
+#endif
+    // 128-offset codes while a weight block meets at most two blocks of 16
+    // activation rows (the per-output fma then costs less than the decode
+    // it saves)
+    constexpr bool OFF = NB <= QG_OFF_NB;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -392,7 +431,7 @@ __global__ void __launch_bounds__(512) qgemm_kernel(GemmParams p) {
                 for (int k = 0; k < XK; k++) {
                     const int kb = step * XK + k;
                     if (!GUARD || kb < nkb) {
-                        const Blk b = F::template block<RA>(rd, hd, kb, q);
+                        const Blk b = F::template block<RA, OFF>(rd, hd, kb, q);
                         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
                         if constexpr (F::TWO) {
                             u32x4 ca, cb;
@@ -422,7 +461,8 @@ __global__ void __launch_bounds__(512) qgemm_kernel(GemmParams p) {
                                     sm = mfma(xl[k][j], ones, sm);
                                 }
 #pragma unroll
-                                for (int i = 0; i < 4; i++) acc[j][i] = fmaf(b.s, d[i], acc[j][i]);
+                                for (int i = 0; i < 4; i++)
+                                    acc[j][i] = fmaf(b.s, off128<F, OFF>(d[i], sm[i]), acc[j][i]);
                                 if constexpr (F::MINS) {
 #pragma unroll
                                     for (int i = 0; i < 4; i++)
@@ -615,7 +655,7 @@ __global__ void __launch_bounds__(512) qgemm8_kernel(GemmParams p) {
 #pragma unroll
             for (int kb = 0; kb < 8; kb++) {
                 if (!GUARD || kb < nkb) {
-                    const Blk bk = F::template block<RA>(rd, hd, kb, q);
+                    const Blk bk = F::template block<RA, true>(rd, hd, kb, q);
                     if constexpr (F::TWO) {
                         u32x4 ca, cb;
 #pragma unroll
@@ -630,10 +670,12 @@ __global__ void __launch_bounds__(512) qgemm8_kernel(GemmParams p) {
                             acc[i] = fmaf(bk.s2, db[i], fmaf(bk.s, da[i], acc[i]));
                     } else {
                         const f32x4 d = mfma(a[kb], bk.c, z);
+                        f32x4 sm = z;
+                        if constexpr (F::MINS) sm = mfma(a[kb], ones, z);
 #pragma unroll
-                        for (int i = 0; i < 4; i++) acc[i] = fmaf(bk.s, d[i], acc[i]);
+                        for (int i = 0; i < 4; i++)
+                            acc[i] = fmaf(bk.s, off128<F, true>(d[i], sm[i]), acc[i]);
                         if constexpr (F::MINS) {
-                            const f32x4 sm = mfma(a[kb], ones, z);
 #pragma unroll
                             for (int i = 0; i < 4; i++) acc[i] = fmaf(-bk.dm, sm[i], acc[i]);
                         }

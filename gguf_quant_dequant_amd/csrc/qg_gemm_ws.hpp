@@ -219,7 +219,7 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
 #pragma unroll
             for (int kb = 0; kb < 8; kb++) {
                 if (!GUARD || kb < nkb) {
-                    const Blk bk = F::template block<RA>(rd, hd, kb, q);
+                    const Blk bk = F::template block<RA, MODE == 0>(rd, hd, kb, q);
                     u32x4 ca = bk.c, cb = bk.c;
                     if constexpr (F::TWO) {
 #pragma unroll
@@ -239,10 +239,12 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
                                     acc[0][i] = fmaf(bk.s2, db[i], fmaf(bk.s, da[i], acc[0][i]));
                             } else {
                                 const f32x4 d = mfma(a, bk.c, z);
+                                f32x4 sm = z;
+                                if constexpr (F::MINS) sm = mfma(a, ones, z);
 #pragma unroll
-                                for (int i = 0; i < 4; i++) acc[0][i] = fmaf(bk.s, d[i], acc[0][i]);
+                                for (int i = 0; i < 4; i++)
+                                    acc[0][i] = fmaf(bk.s, gm::off128<F, MODE == 0>(d[i], sm[i]), acc[0][i]);
                                 if constexpr (F::MINS) {
-                                    const f32x4 sm = mfma(a, ones, z);
 #pragma unroll
                                     for (int i = 0; i < 4; i++)
                                         acc[0][i] = fmaf(-bk.dm, sm[i], acc[0][i]);
@@ -262,11 +264,15 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
                             } else {
                                 f32x4 d = mfma(ah, bk.c, z);
                                 d = mfma(al2, bk.c, d);
-#pragma unroll
-                                for (int i = 0; i < 4; i++) acc[j][i] = fmaf(bk.s, d[i], acc[j][i]);
+                                f32x4 sm = z;
                                 if constexpr (F::MINS) {
-                                    f32x4 sm = mfma(ah, ones, z);
+                                    sm = mfma(ah, ones, z);
                                     sm = mfma(al2, ones, sm);
+                                }
+#pragma unroll
+                                for (int i = 0; i < 4; i++)
+                                    acc[j][i] = fmaf(bk.s, gm::off128<F, MODE == 0>(d[i], sm[i]), acc[j][i]);
+                                if constexpr (F::MINS) {
 #pragma unroll
                                     for (int i = 0; i < 4; i++)
                                         acc[j][i] = fmaf(-bk.dm, sm[i], acc[j][i]);

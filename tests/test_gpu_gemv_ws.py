@@ -131,3 +131,32 @@ def test_run_to_run_bitwise_identical():
     a, _ = run_ws(Q5_K, W, rows, cols, X)
     b, _ = run_ws(Q5_K, W, rows, cols, X, ws_pad=64)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", [Q4_K, Q5_K])
+@pytest.mark.parametrize("batch", [2, 4, 8, 16, 32])
+def test_k_quant_rows_of_zero_weights_give_zero(fmt, batch):
+    # every super-block of every third row: nonzero d and sub-block scales,
+    # dmin = 0 and all codes 0, so every weight is 0 and the output must be
+    # 0 (the codes enter the matrix core as 128 + q; the 128 offset must
+    # cancel exactly), through qgemv and qgemv_ws
+    rows, cols = 150, 2048
+    W = synth.matrix(synth.rng(8600 + fmt + batch), fmt, rows, cols)
+    rb = q.qg_row_bytes(fmt, cols)
+    bb = 144 if fmt == Q4_K else 176
+    Wr = W.reshape(rows, rb)
+    zero_rows = np.arange(0, rows, 3)
+    for sb in range(cols // 256):
+        o = sb * bb
+        Wr[zero_rows, o + 2:o + 4] = 0          # dmin
+        Wr[zero_rows, o + 16:o + bb] = 0        # (qh and) qs
+    X = synth.activations(synth.rng(8700 + batch), batch, cols)
+    Yr, A = oracle.gemv(fmt, W, rows, cols, X)
+    assert np.all(Yr[:, zero_rows] == 0)
+    Y, _ = run_ws(fmt, W, rows, cols, X)
+    assert np.all(np.abs(Y[:, zero_rows]) <= 1e-6), np.abs(Y[:, zero_rows]).max()
+    assert_agree(Y, Yr, A, f"ws zero rows fmt {fmt} b{batch}")
+    from gpu_util import run_gemv
+    Y2 = run_gemv(fmt, W, rows, cols, X)
+    assert np.all(np.abs(Y2[:, zero_rows]) <= 1e-6), np.abs(Y2[:, zero_rows]).max()
+    assert_agree(Y2, Yr, A, f"qgemv zero rows fmt {fmt} b{batch}")
