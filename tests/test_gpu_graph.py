@@ -173,3 +173,28 @@ def test_q8act_and_sliced_gemv_graph_replays_match_eager():
         q.qgemv(q.QG_Q5_K, Ws, 8200, 4096, Xs, Ys, 8)
 
     _replays_match(run, [yq, Ys], "q8act + slices")
+
+
+def test_qgemv_ws_graph_replays_match_eager():
+    # the shared-operand kernel with its column ranges summed by the second
+    # kernel (workspace written whole on every call), at batch 8 (packed
+    # operands), 24 (two blocks of 16 rows) and 40 (two launches)
+    g = synth.rng(995)
+    cases = [(q.QG_Q5_K, 1000, 4096, 8), (q.QG_Q4_0, 300, 4096, 24), (q.QG_Q4_K, 200, 4096, 40)]
+    bufs = []
+    for fmt, rows, cols, b in cases:
+        W = torch.from_numpy(synth.matrix(g, fmt, rows, cols).reshape(-1)).cuda()
+        X = torch.from_numpy(synth.activations(g, b, cols)).cuda()
+        need = q.qgemv_ws_bytes(fmt, rows, cols, b)
+        assert need > 0
+        ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+        bufs.append((fmt, rows, cols, b, W, X, ws, torch.empty(b, rows, device="cuda")))
+
+    def run():
+        for fmt, rows, cols, b, W, X, ws, Y in bufs:
+            q.qgemv_ws(fmt, W, rows, cols, X, Y, b, ws)
+
+    # the workspaces are overwritten before each replay too: nothing may
+    # depend on what an earlier call left there
+    outs = [Y for *_, Y in bufs] + [ws for *_, ws, _ in bufs]
+    _replays_match(run, outs, "qgemv_ws")
