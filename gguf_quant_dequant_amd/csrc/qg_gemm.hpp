@@ -279,6 +279,18 @@ struct GQ6K {
     }
 };
 
+// Cache policy of the batched kernels' weight loads: the default (0), not
+// the non-temporal policy of the contiguous batch-1 streams.  A 16-row tile
+// reads 144-272-byte row segments chunk by chunk, and consecutive chunks
+// share the lines at their boundaries; with non-temporal loads those lines
+// were fetched twice.  Measured at batch 8 (cold weights): Q4_0 4096 x 14336
+// 44.2 -> 39.4 MB read, 23.0 -> 22.7 us; Q5_K 14336 x 4096 44.7 -> 43.4 MB,
+// 25.1 -> 24.7 us.  (The shared-operand kernel keeps the non-temporal
+// policy: there it read fewer bytes but ran no faster, Q4_0 slower.)
+#ifndef QG_GEMM_AUX
+#define QG_GEMM_AUX 0
+#endif
+
 // ---------------------------------------------------------------- kernel
 
 // A block's product sum with the codes' 128 offset removed (formats with
@@ -370,7 +382,7 @@ __global__ void __launch_bounds__(512) qgemm_kernel(GemmParams p) {
                     (d0 + u_row[j] * p.row_bytes + (uint32_t)c * F::CHUNK) & ~15u;
                 const uint32_t off = lane + 64 * j < nunits ? base + u_off[j] : 0xFFFFFFF0u;
                 wreg[j] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStream));
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, QG_GEMM_AUX));
             }
         };
         // the chunk's rows into the wave's LDS slot (the previous chunk's
@@ -580,7 +592,7 @@ __global__ void __launch_bounds__(512) qgemm8_kernel(GemmParams p) {
                 const uint32_t off =
                     valid && lane + 64 * j < nunits ? base + u_off[j] : 0xFFFFFFF0u;
                 w[j] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, kStream));
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, QG_GEMM_AUX));
             }
         };
         auto w_store = [&](const u32x4 (&w)[UNITS]) {
