@@ -472,6 +472,8 @@ ARITH = {
     "mfma_bf16": "bf16 codes x bf16 hi + lo activation parts on the matrix cores, f32 sums",
     "mfma_bf16_ws": "bf16 codes x bf16 hi + lo activation parts on the matrix cores, f32 sums, "
                     "column ranges added in a second kernel",
+    "mfma_bf16_ks2": "bf16 codes x bf16 hi + lo activation parts on the matrix cores, f32 sums, "
+                     "activations shared by 4 row tiles, two column ranges added in the workgroup",
     "q8act": "int8 codes x int8 activations (per 16 columns), exact int32 sums, f32 per group",
     "moe": "f64 router, f32 expert GEMVs on the vector ALUs",
     "moe_q8": "f64 router, expert GEMVs as int8 codes x int8 activations (per 16 columns), "
@@ -484,7 +486,8 @@ def gemv_arith(q):
     """The arithmetic the library reports for its last GEMV call."""
     return ARITH[{"valu_f32": "valu_f32", "valu_q6k_int": "valu_q6k_int",
                   "mfma_i8_q6k": "mfma_i8_q6k", "mx_f16": "mfma_f16", "gemm_bf16": "mfma_bf16",
-                  "gemm_ws_bf16": "mfma_bf16_ws", "valu_q8act": "q8act"}[q.qg_last_kernel()]]
+                  "gemm_ws_bf16": "mfma_bf16_ws", "gemm_ks2_bf16": "mfma_bf16_ks2",
+                  "valu_q8act": "q8act"}[q.qg_last_kernel()]]
 
 
 def main():

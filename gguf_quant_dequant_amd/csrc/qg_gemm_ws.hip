@@ -19,15 +19,35 @@
 namespace qg {
 namespace host {
 
-// Column ranges per group of 8 tiles: as many as keep the grid within
-// QG_WS_WGS workgroups.  Independent of the device, so the workspace size is
-// known on the host before any call.
-int ws_kg(int64_t rows, int64_t cols) {
+// Two column ranges inside each workgroup of 4 tiles (added in LDS) for
+// tall matrices at batch 8 or less: at least QG_KS2_MIN_WGS such
+// workgroups (one per CU of a 256-CU part, and more) and 4 chunks per row,
+// so that no range is split across workgroups.  Measured at batch 4 / 8,
+// cold weights: Q5_K 14336 x 4096 18.4 / 18.9 us with 8 tiles per
+// workgroup and two ranges across workgroups, 16.7 / 18.0 us with the two
+// ranges inside; Q4_0 4096 x 14336 (64 such workgroups) slower with them,
+// 18.6 / 18.7 -> 18.9 / 20.5 us, so short matrices keep the split across
+// workgroups.
+#ifndef QG_KS2_MIN_WGS
+#define QG_KS2_MIN_WGS 192
+#endif
+static int ws_ks(int64_t rows, int64_t cols, int batch) {
     const int64_t tiles = (rows + gm::kTileRows - 1) / gm::kTileRows;
-    const int64_t groups = (tiles + gw::kWaves - 1) / gw::kWaves;
+    const int64_t groups = (tiles + gw::kWaves / 2 - 1) / (gw::kWaves / 2);
+    const int64_t nchunks = (cols + gm::kChunk - 1) / gm::kChunk;
+    return batch <= 8 && QG_KS2_MIN_WGS > 0 && groups >= QG_KS2_MIN_WGS && nchunks >= 4 ? 2 : 1;
+}
+
+// Column ranges across workgroups per group of tiles: as many as keep the
+// grid within QG_WS_WGS workgroups.  Independent of the device, so the
+// workspace size is known on the host before any call.
+int ws_kg(int64_t rows, int64_t cols, int batch) {
+    const int ks = ws_ks(rows, cols, batch), tpg = gw::kWaves / ks;
+    const int64_t tiles = (rows + gm::kTileRows - 1) / gm::kTileRows;
+    const int64_t groups = (tiles + tpg - 1) / tpg;
     const int64_t nchunks = (cols + gm::kChunk - 1) / gm::kChunk;
     int64_t kg = QG_WS_WGS / groups;
-    const int64_t cap = nchunks / QG_WS_MIN_CHUNKS;
+    const int64_t cap = nchunks / (QG_WS_MIN_CHUNKS * ks);
     if (kg > cap) kg = cap;
     if (kg < 1) kg = 1;
     return (int)kg;
@@ -35,11 +55,11 @@ int ws_kg(int64_t rows, int64_t cols) {
 
 namespace {
 
-template <class F, int MODE, bool RA>
+template <class F, int MODE, bool RA, int KS = 1>
 int launch_ws_t(const gw::WsParams &p, hipStream_t st) {
     constexpr int U = gemm_units(F::CHUNK);
-    auto kern = gw::qgemm_ws_kernel<F, MODE, RA, U>;
-    const size_t lds = gw::ws_lds_bytes<MODE>(p.slot);
+    auto kern = gw::qgemm_ws_kernel<F, MODE, RA, U, KS>;
+    const size_t lds = gw::ws_lds_bytes<MODE, KS>(p.slot);
     if (lds > (size_t)device_lds_max())
         return fail(QG_EUNSUPPORTED, "qgemv_ws: %zu bytes of LDS per workgroup exceed the "
                                      "device's %d", lds, device_lds_max());
@@ -50,7 +70,7 @@ int launch_ws_t(const gw::WsParams &p, hipStream_t st) {
         (void)hipGetLastError();
         attr.store(true, std::memory_order_relaxed);
     }
-    const int64_t groups = ((int64_t)p.tiles + gw::kWaves - 1) / gw::kWaves;
+    const int64_t groups = ((int64_t)p.tiles + gw::kWaves / KS - 1) / (gw::kWaves / KS);
     hipLaunchKernelGGL(kern, dim3((unsigned)(groups * p.kg)), dim3(gw::kThreads), lds, st, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -68,9 +88,11 @@ int launch_ws_t(const gw::WsParams &p, hipStream_t st) {
     return QG_OK;
 }
 
-template <class F>
+// KS = 2: two column ranges inside each workgroup of 4 tiles and no split
+// across workgroups (no workspace; batch <= 8).
+template <class F, int KS = 1>
 int launch_ws(const void *W, int64_t rows, int64_t cols, const float *X, float *Y, int batch,
-              int64_t rb, float *part, hipStream_t st) {
+              int64_t rb, float *part, int kg, hipStream_t st) {
     gw::WsParams p{};
     p.W = (const uint8_t *)W;
     p.X = X;
@@ -84,12 +106,17 @@ int launch_ws(const void *W, int64_t rows, int64_t cols, const float *X, float *
     p.nchunks = (int32_t)((cols + gm::kChunk - 1) / gm::kChunk);
     p.last_nkb = (int32_t)(((cols - 1) % gm::kChunk) / 32 + 1);
     p.tiles = (int32_t)((rows + gm::kTileRows - 1) / gm::kTileRows);
-    p.kg = ws_kg(rows, cols);
+    p.kg = kg;
     p.nu = gemm_nu(F::CHUNK);
     p.slot = 16u * (uint32_t)(p.nu | 1);
     // 4-byte-aligned fields in LDS when every row and chunk starts at a
     // multiple of 4 bytes
     const bool ra = !(F::CHUNK % 4 == 0 && rb % 4 == 0 && aligned_to(W, 4));
+    if constexpr (KS == 2) {
+        if constexpr (F::CHUNK % 4 == 0)
+            if (!ra) return launch_ws_t<F, 0, false, 2>(p, st);
+        return launch_ws_t<F, 0, true, 2>(p, st);
+    }
     if constexpr (F::CHUNK % 4 == 0) {
         if (!ra) {
             if (batch <= 8) return launch_ws_t<F, 0, false>(p, st);
@@ -104,16 +131,40 @@ int launch_ws(const void *W, int64_t rows, int64_t cols, const float *X, float *
 
 }  // namespace
 
+// qgemv takes the two-range kernel where qgemv_ws would (no workspace is
+// needed there); shorter matrices keep qgemm8_kernel.
+bool gemm_ks2_fits(int fmt, int64_t rows, int64_t cols, int batch) {
+    return fmt != QG_F32 && batch >= 2 && ws_ks(rows, cols, batch) == 2;
+}
+
+int gemm_ks2(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
+             int batch, int64_t rb, hipStream_t st) {
+    switch (fmt) {
+    case QG_Q4_K: return launch_ws<gm::GK45<false>, 2>(W, rows, cols, X, Y, batch, rb, nullptr, 1, st);
+    case QG_Q5_K: return launch_ws<gm::GK45<true>, 2>(W, rows, cols, X, Y, batch, rb, nullptr, 1, st);
+    case QG_Q6_K: return launch_ws<gm::GQ6K, 2>(W, rows, cols, X, Y, batch, rb, nullptr, 1, st);
+    case QG_Q8_0: return launch_ws<gm::GQ80, 2>(W, rows, cols, X, Y, batch, rb, nullptr, 1, st);
+    case QG_Q4_0: return launch_ws<gm::GQ40, 2>(W, rows, cols, X, Y, batch, rb, nullptr, 1, st);
+    default: return fail(QG_EUNSUPPORTED, "qgemv: format %d has no matrix-core path", fmt);
+    }
+}
+
 int gemm_ws(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
             int batch, int64_t rb, float *part, hipStream_t st) {
+    const int kg = ws_kg(rows, cols, batch);
+    const bool two = ws_ks(rows, cols, batch) == 2;
+#define QG_WS_CASE(F)                                                                        \
+    return two ? launch_ws<F, 2>(W, rows, cols, X, Y, batch, rb, part, kg, st)              \
+               : launch_ws<F, 1>(W, rows, cols, X, Y, batch, rb, part, kg, st)
     switch (fmt) {
-    case QG_Q4_K: return launch_ws<gm::GK45<false>>(W, rows, cols, X, Y, batch, rb, part, st);
-    case QG_Q5_K: return launch_ws<gm::GK45<true>>(W, rows, cols, X, Y, batch, rb, part, st);
-    case QG_Q6_K: return launch_ws<gm::GQ6K>(W, rows, cols, X, Y, batch, rb, part, st);
-    case QG_Q8_0: return launch_ws<gm::GQ80>(W, rows, cols, X, Y, batch, rb, part, st);
-    case QG_Q4_0: return launch_ws<gm::GQ40>(W, rows, cols, X, Y, batch, rb, part, st);
+    case QG_Q4_K: QG_WS_CASE(gm::GK45<false>);
+    case QG_Q5_K: QG_WS_CASE(gm::GK45<true>);
+    case QG_Q6_K: QG_WS_CASE(gm::GQ6K);
+    case QG_Q8_0: QG_WS_CASE(gm::GQ80);
+    case QG_Q4_0: QG_WS_CASE(gm::GQ40);
     default: return fail(QG_EUNSUPPORTED, "qgemv_ws: format %d has no matrix-core path", fmt);
     }
+#undef QG_WS_CASE
 }
 
 }  // namespace host

@@ -59,40 +59,54 @@ struct WsParams {
 // Operand planes per image: MODE 0 one (hi and lo packed), 1 two (hi, lo),
 // 2 four (hi, lo of each block of 16 batch rows).  An image plane holds the
 // 8 blocks' operands of one chunk, 64 lanes x 16 bytes each.
-template <int MODE>
+// KS: column ranges inside a workgroup.  With KS = 2 the workgroup holds 4
+// tiles, waves 0-3 take the first half of each row's chunks and waves 4-7
+// the second, each half with its own activation images, and the halves'
+// sums are added through LDS at the end (no workspace).
+template <int MODE, int KS = 1>
 struct Mode {
     static constexpr int PLANES = MODE == 0 ? 1 : MODE == 1 ? 2 : 4;
     static constexpr int MAXB = MODE == 0 ? 8 : MODE == 1 ? 16 : 32;
-    static constexpr int XU = (MAXB * 64 + kThreads - 1) / kThreads;  // activation units per thread
-    static constexpr uint32_t IMG_U32 = PLANES * 8 * 64 * 4;         // one image, in dwords
+    static constexpr int TH = kThreads / KS;                    // threads per column range
+    static constexpr int XU = (MAXB * 64 + TH - 1) / TH;        // activation units per thread
+    static constexpr uint32_t IMG_U32 = PLANES * 8 * 64 * 4;   // one image, in dwords
 };
 
-// Bytes of LDS a workgroup uses: two activation images, the waves' weight
-// slots.
-template <int MODE>
+// Bytes of LDS a workgroup uses: two activation images per column range,
+// the waves' weight slots.
+template <int MODE, int KS = 1>
 __host__ __device__ constexpr size_t ws_lds_bytes(uint32_t slot) {
-    return 2 * (size_t)Mode<MODE>::IMG_U32 * 4 + (size_t)kWaves * kTileRows * slot;
+    return 2 * KS * (size_t)Mode<MODE>::IMG_U32 * 4 + (size_t)kWaves * kTileRows * slot;
 }
 
-template <class F, int MODE, bool RA, int UNITS>
+template <class F, int MODE, bool RA, int UNITS, int KS = 1>
 __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
-    using M = Mode<MODE>;
+    using M = Mode<MODE, KS>;
+    static_assert(KS == 1 || KS == 2, "one or two column ranges per workgroup");
+    constexpr int TPG = kWaves / KS;  // tiles per workgroup
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    uint32_t *img = (uint32_t *)smem;  // [2][PLANES][8][64][4]
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int half = wave / TPG;          // this wave's column range in the workgroup
+    const int htid = tid - half * M::TH;  // thread index inside that range's waves
+    uint32_t *img = (uint32_t *)smem + (uint32_t)half * 2 * M::IMG_U32;  // [2][PLANES][8][64][4]
     const int r = lane & 15, q = lane >> 4;
     const int group = (int)(blockIdx.x / (uint32_t)p.kg);
     const int kgi = (int)(blockIdx.x % (uint32_t)p.kg);
-    const int64_t tile = (int64_t)group * kWaves + wave;
+    const int64_t tile = (int64_t)group * TPG + wave % TPG;
     const bool has_tile = tile < p.tiles;
-    const int c0 = (int)((int64_t)kgi * p.nchunks / p.kg);
-    const int c1 = (int)((int64_t)(kgi + 1) * p.nchunks / p.kg);
-    uint8_t *stage = smem + 2 * (size_t)M::IMG_U32 * 4 + (size_t)wave * kTileRows * p.slot;
+    // column range kgi * KS + half of kg * KS; every range of the workgroup
+    // runs the same number of steps (the longest range's), so that the
+    // barriers match
+    const int nr = p.kg * KS, ri = kgi * KS + half;
+    const int c0 = (int)((int64_t)ri * p.nchunks / nr);
+    const int c1 = (int)((int64_t)(ri + 1) * p.nchunks / nr);
+    const int nsteps = (p.nchunks + nr - 1) / nr;
+    uint8_t *stage = smem + 2 * KS * (size_t)M::IMG_U32 * 4 + (size_t)wave * kTileRows * p.slot;
 
-    // zero both images: rows past the batch are never written and read as 0
-    for (uint32_t i = (uint32_t)tid; i < 2 * M::IMG_U32 / 4; i += kThreads)
-        ((u32x4 *)img)[i] = u32x4{0u, 0u, 0u, 0u};
+    // zero the images: rows past the batch are never written and read as 0
+    for (uint32_t i = (uint32_t)tid; i < 2 * KS * M::IMG_U32 / 4; i += kThreads)
+        ((u32x4 *)smem)[i] = u32x4{0u, 0u, 0u, 0u};
 
     // ---- activations: unit u of a chunk is four columns of one batch row
     const rsrc_t rx = make_rsrc(p.X, 4u * p.cols * (uint32_t)p.batch);
@@ -102,7 +116,7 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
     auto x_issue = [&](int c, uint32_t (&x)[M::XU][4], bool valid) {
 #pragma unroll
         for (int j = 0; j < M::XU; j++) {
-            const int u = tid + kThreads * j;
+            const int u = htid + M::TH * j;
             const int b = u >> 6;
             const uint32_t col = (uint32_t)c * kChunk + 4u * (uint32_t)(u & 63);
             const uint32_t off = (valid && b < p.batch && col < p.cols)
@@ -118,7 +132,7 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
     auto x_commit = [&](int buf, const uint32_t (&x)[M::XU][4]) {
 #pragma unroll
         for (int j = 0; j < M::XU; j++) {
-            const int u = tid + kThreads * j;
+            const int u = htid + M::TH * j;
             const int b = u >> 6;
             if (b < p.batch) {
                 const int c4 = 4 * (u & 63);
@@ -206,9 +220,10 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
     // barrier.  GUARD: the row's last chunk may hold fewer than 8 blocks.
     auto chunk = [&](int c, u32x4 (&wc)[UNITS], uint32_t (&xn)[M::XU][4], auto guard_tag) {
         constexpr bool GUARD = decltype(guard_tag)::value;
-        w_store(wc);
+        const bool live = !GUARD || c < c1;  // a step past a shorter range computes nothing
+        if (live) w_store(wc);
         w_issue(c + 2, wc, c + 2 < c1);
-        if (has_tile) {
+        if (has_tile && live) {
             const int nkb = GUARD && c == p.nchunks - 1 ? p.last_nkb : 8;
             const uint32_t delta =
                 (d0 + (uint32_t)r * p.row_bytes + (uint32_t)c * F::CHUNK) & 15u;
@@ -292,26 +307,28 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
     // c0 & 1, c0 + 2's activations in flight
     uint32_t xA[M::XU][4], xB[M::XU][4];
     u32x4 wA[UNITS], wB[UNITS];
-    x_issue(c0, xA, true);
-    w_issue(c0, wA, true);
+    x_issue(c0, xA, c0 < c1);
+    w_issue(c0, wA, c0 < c1);
     x_issue(c0 + 1, xB, c0 + 1 < c1);
     w_issue(c0 + 1, wB, c0 + 1 < c1);
     __syncthreads();  // the images are zero
-    x_commit(c0 & 1, xA);
+    if (c0 < c1) x_commit(c0 & 1, xA);
     x_issue(c0 + 2, xA, c0 + 2 < c1);
     __syncthreads();
     // chunk c's successor's activations are in xB for even c - c0, xA for
-    // odd; the weights of c in wA for even c - c0, wB for odd
-    int c = c0;
-    for (; c + 2 < c1; c += 2) {
-        chunk(c, wA, xB, std::false_type{});
-        chunk(c + 1, wB, xA, std::false_type{});
+    // odd; the weights of c in wA for even c - c0, wB for odd.  The last one
+    // or two steps take the variant that checks for the end of the range and
+    // for a partial last chunk.
+    int s = 0;
+    for (; s + 2 < nsteps; s += 2) {
+        chunk(c0 + s, wA, xB, std::false_type{});
+        chunk(c0 + s + 1, wB, xA, std::false_type{});
     }
-    if (c + 1 == c1) {
-        chunk(c, wA, xB, std::true_type{});
+    if (s + 1 == nsteps) {
+        chunk(c0 + s, wA, xB, std::true_type{});
     } else {
-        chunk(c, wA, xB, std::false_type{});
-        chunk(c + 1, wB, xA, std::true_type{});
+        chunk(c0 + s, wA, xB, std::true_type{});
+        chunk(c0 + s + 1, wB, xA, std::true_type{});
     }
 
     if constexpr (MODE == 0) {
@@ -319,6 +336,24 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
         // parts' sums lane (r, q) holds
 #pragma unroll
         for (int i = 0; i < 4; i++) acc[0][i] += __shfl_xor(acc[0][i], 32);
+    }
+    if constexpr (KS == 2) {
+        // the second range's waves hand their sums to the first range's
+        // waves of the same tile through LDS (the images are free after the
+        // last step's barrier), which add them in range order
+        f32x4 *xch = (f32x4 *)smem + ((wave % TPG) * NBB) * 64 + lane;
+        if (half == 1) {
+#pragma unroll
+            for (int j = 0; j < NBB; j++) xch[j * 64] = acc[j];
+        }
+        __syncthreads();
+        if (half == 1) return;
+#pragma unroll
+        for (int j = 0; j < NBB; j++) {
+            const f32x4 o = xch[j * 64];
+#pragma unroll
+            for (int i = 0; i < 4; i++) acc[j][i] += o[i];
+        }
     }
     const int64_t row = tile * kTileRows + r;
     if (has_tile && row < p.rows && (MODE != 0 || q < 2)) {

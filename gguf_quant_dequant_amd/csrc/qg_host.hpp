@@ -287,7 +287,10 @@ int dispatch_down(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_gateup_q8(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_down_q8(int fmt, const MoeParams &p, hipStream_t st);
 int try_q6mx(const GemvParams &p, hipStream_t st, bool *done);
-int ws_kg(int64_t rows, int64_t cols);
+int ws_kg(int64_t rows, int64_t cols, int batch);
+bool gemm_ks2_fits(int fmt, int64_t rows, int64_t cols, int batch);
+int gemm_ks2(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
+             int batch, int64_t rb, hipStream_t st);
 int gemm_ws(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
             int batch, int64_t rb, float *part, hipStream_t st);
 

@@ -120,6 +120,9 @@ const char *qg_last_error(void);
  *   "gemm_bf16"     matrix cores, bf16 codes x bf16 hi + lo activation parts;
  *   "gemm_ws_bf16"  the same arithmetic, activation operands shared through
  *                   LDS (qgemv_ws);
+ *   "gemm_ks2_bf16" the same arithmetic, activation operands shared through
+ *                   LDS by 4 row tiles, two column ranges per workgroup
+ *                   added in LDS (qgemv, batch 2-8, tall matrices);
  *   "valu_q8act"    int8 codes x int8 activations (qgemv_q8act).
  * A static string; reporting only, no effect on any call. */
 const char *qg_last_kernel(void);
@@ -156,11 +159,16 @@ const char *qg_last_kernel(void);
  * bit for bit in int32.  At batch >= 2 (and for batch-1 rows wider than 512 lane tiles)
  * the block formats run on the matrix cores with the codes as exact
  * integers (codes at a format's zero point are exact zeros) and f32 sums:
- * at batch 2..4 when the activations fit in LDS, and for the over-wide
- * batch-1 rows, as f16 codes with each 256-column chunk of X split into
- * f16 hi + lo parts after a power-of-two scaling (relative error < 2^-21
- * per element); otherwise as bf16 codes with X split into bf16 hi + lo
- * parts (relative error <= 2^-16 per element).  qg_last_kernel() names the
+ * at batch 2..4 when the activations fit in LDS (and the matrix is not
+ * tall enough for the shared-activation kernel below), and for the
+ * over-wide batch-1 rows, as f16 codes with each 256-column chunk of X
+ * split into f16 hi + lo parts after a power-of-two scaling (relative
+ * error < 2^-21 per element); otherwise as bf16 codes with X split into
+ * bf16 hi + lo parts (relative error <= 2^-16 per element).  At batch 2..8
+ * matrices of at least 192 groups of 4 row tiles (12,241 rows or more) and
+ * 4 or more 256-column chunks run on a kernel whose workgroups share each
+ * activation chunk between 4 row tiles through LDS and add two column
+ * ranges in LDS ("gemm_ks2_bf16", no workspace).  qg_last_kernel() names the
  * arithmetic a call used.  Results are
  * deterministic run to run.  Limits: rows < 2^31, cols <= 65536; rows that fit neither
  * kernel (e.g. more than ~64 chunks of 256 columns at batch 1 beyond 512
@@ -180,7 +188,10 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
  * row's columns are split over several workgroups; their partial sums go
  * to the workspace and a second kernel adds them per output in a fixed
  * order, so results are deterministic run to run (they differ from
- * qgemv's in rounding only).  F32 and batch 1 run qgemv itself.
+ * qgemv's in rounding only).  At batch 2..8 the matrices on which qgemv
+ * runs "gemm_ks2_bf16" (4 row tiles per workgroup, two column ranges added
+ * in LDS) take that kernel here too, with no workspace (qgemv_ws_bytes 0).
+ * F32 and batch 1 run qgemv itself.
  *
  *   workspace        device memory of at least qgemv_ws_bytes(fmt, rows,
  *                    cols, batch) bytes, 16-byte aligned, owned by the
@@ -198,7 +209,7 @@ int qgemv_ws(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
              void *stream);
 
 /* Workspace bytes qgemv_ws needs for these arguments: 0 when none is needed
- * (F32, batch 1, a row split over a single workgroup) and for arguments
+ * (F32, batch 1, no row split over several workgroups) and for arguments
  * qgemv_ws refuses.  Depends only on the arguments, not on the device. */
 size_t qgemv_ws_bytes(int fmt, int64_t rows, int64_t cols, int batch);
 
