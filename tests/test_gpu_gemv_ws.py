@@ -7,7 +7,8 @@ rows above), row counts with a partial last group of 8 tiles and a partial
 last tile, rows split over several workgroups (the workspace path) and over
 one (no workspace), a partial last chunk of 256 columns, weights 2 bytes
 past 4-byte alignment, the workload shapes at full size on sampled rows,
-the workspace checks, and run-to-run determinism.  Tolerance as for every
+the workspace checks, one workspace reused by calls of other shapes, and
+run-to-run determinism.  Tolerance as for every
 GEMV: |y - y_ref| <= 1e-4 * sum|w x| + 1e-6 per output.
 """
 from __future__ import annotations
@@ -160,3 +161,22 @@ def test_k_quant_rows_of_zero_weights_give_zero(fmt, batch):
     Y2 = run_gemv(fmt, W, rows, cols, X)
     assert np.all(np.abs(Y2[:, zero_rows]) <= 1e-6), np.abs(Y2[:, zero_rows]).max()
     assert_agree(Y2, Yr, A, f"qgemv zero rows fmt {fmt} b{batch}")
+
+
+def test_one_workspace_reused_by_calls_of_other_shapes():
+    # no initial contents needed: one workspace of garbage bytes serves calls
+    # of other shapes and sizes one after another
+    shapes = [(Q4_0, 300, 4096, 8), (Q4_K, 1000, 4096, 4), (Q5_K, 150, 2048, 16),
+              (Q4_0, 300, 4096, 8), (Q6_K, 600, 4096, 40), (Q4_K, 1000, 4096, 4)]
+    need = max(q.qgemv_ws_bytes(f, r, c, b) for f, r, c, b in shapes)
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=dev())
+    for i, (fmt, rows, cols, batch) in enumerate(shapes):
+        W = synth.matrix(synth.rng(8800 + i), fmt, rows, cols)
+        X = synth.activations(synth.rng(8900 + i), batch, cols)
+        Wd = DeviceBytes(W)
+        Xd = torch.from_numpy(X).to(dev())
+        Y = torch.full((batch, rows), float("nan"), device=dev())
+        q.qgemv_ws(fmt, Wd.ptr, rows, cols, Xd, Y, batch, ws, need)
+        torch.cuda.synchronize()
+        Yr, A = oracle.gemv(fmt, W, rows, cols, X)
+        assert_agree(Y.cpu().numpy(), Yr, A, f"reused workspace, call {i}")
