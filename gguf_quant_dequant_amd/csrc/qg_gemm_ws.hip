@@ -149,6 +149,74 @@ int gemm_ks2(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
     }
 }
 
+// The gate and up products of T <= 8 MoE tokens on the shared-activation
+// kernel: every workgroup routes the tokens (or, with rt, reads the routing
+// done ahead), then takes 4 pairs of gate / up tiles of the distinct experts
+// (at most T * K of them) with SwiGLU in the epilogue.
+template <class F>
+int launch_moe_ws(const uint8_t *gate, const uint8_t *up, uint64_t stack_bytes, int64_t rb,
+                  int H, int F_, int K, int T, int E, const float *x, const double *logits,
+                  const int32_t *rt, int32_t *sel, float *rw, int32_t *sel_out, float *w_out,
+                  float *act, hipStream_t st) {
+    gw::WsParams p{};
+    p.W = gate;
+    p.W2 = up;
+    p.X = x;
+    p.w_bytes = stack_bytes;
+    p.row_bytes = (uint32_t)rb;
+    p.cols = (uint32_t)H;
+    p.batch = T;
+    p.nchunks = (int32_t)((H + gm::kChunk - 1) / gm::kChunk);
+    p.last_nkb = (int32_t)(((H - 1) % gm::kChunk) / 32 + 1);
+    p.kg = 1;
+    p.nu = gemm_nu(F::CHUNK);
+    p.slot = 16u * (uint32_t)(p.nu | 1);
+    p.logits = logits;
+    p.rt = rt;
+    p.sel = sel;
+    p.rw = rw;
+    p.sel_out = sel_out;
+    p.w_out = w_out;
+    p.act = act;
+    p.E = E;
+    p.F = F_;
+    p.K = K;
+    p.tpe = F_ / gm::kTileRows;
+    // every distinct expert's gate and up tiles, for the largest possible
+    // count of distinct experts; workgroups past the actual count return
+    const int64_t pairs = (int64_t)T * K * p.tpe;
+    p.tiles = (int32_t)(2 * pairs);
+    const int64_t grid = (pairs + gw::kWaves / 2 - 1) / (gw::kWaves / 2);
+    const bool ra = !(F::CHUNK % 4 == 0 && rb % 4 == 0 && aligned_to(gate, 4) && aligned_to(up, 4));
+    constexpr int U = gemm_units(F::CHUNK);
+    auto kern = ra ? gw::qgemm_ws_kernel<F, 0, true, U, 1, true>
+                   : gw::qgemm_ws_kernel<F, 0, F::CHUNK % 4 != 0, U, 1, true>;
+    const size_t lds = gw::ws_lds_bytes<0, 1>(p.slot);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(gw::kThreads), lds, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return fail(QG_ELAUNCH, "moe_ffn_tokens: gate/up launch failed: %s", hipGetErrorString(e));
+    return QG_OK;
+}
+
+int moe_gateup_ws(int fmt, const uint8_t *gate, const uint8_t *up, uint64_t stack_bytes,
+                  int64_t rb, int H, int F, int K, int T, int E, const float *x,
+                  const double *logits, const int32_t *rt, int32_t *sel, float *rw,
+                  int32_t *sel_out, float *w_out, float *act, hipStream_t st) {
+#define QG_MOE_WS_CASE(FM)                                                                   \
+    return launch_moe_ws<FM>(gate, up, stack_bytes, rb, H, F, K, T, E, x, logits, rt, sel,   \
+                             rw, sel_out, w_out, act, st)
+    switch (fmt) {
+    case QG_Q4_K: QG_MOE_WS_CASE(gm::GK45<false>);
+    case QG_Q5_K: QG_MOE_WS_CASE(gm::GK45<true>);
+    case QG_Q6_K: QG_MOE_WS_CASE(gm::GQ6K);
+    case QG_Q8_0: QG_MOE_WS_CASE(gm::GQ80);
+    case QG_Q4_0: QG_MOE_WS_CASE(gm::GQ40);
+    default: return fail(QG_EUNSUPPORTED, "moe_ffn_tokens: gate/up format %d", fmt);
+    }
+#undef QG_MOE_WS_CASE
+}
+
 int gemm_ws(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
             int batch, int64_t rb, float *part, hipStream_t st) {
     const int kg = ws_kg(rows, cols, batch);

@@ -23,6 +23,7 @@
 #pragma once
 
 #include "qg_gemm.hpp"
+#include "qg_kernels.hpp"
 
 namespace qg {
 namespace gw {
@@ -54,6 +55,21 @@ struct WsParams {
     int32_t kg;         // column ranges (workgroups per group of 8 tiles)
     int32_t nu;         // 16-byte units staged per row segment
     uint32_t slot;      // LDS bytes per staged row (odd multiple of 16)
+    // the grouped gate/up products of several MoE tokens (MOE kernels): W is
+    // the gate stack, W2 the up stack (w_bytes each), X the T = batch tokens'
+    // activations, logits their router logits [T][E]; the routes and route
+    // weights [T][K] are written to sel and rw (and sel_out, w_out when
+    // given), the SwiGLU activations [T][K][F] to act.  With rt set the
+    // routing has been done (moe_route_tokens_kernel): rt holds the distinct
+    // experts, their slots per token and their count (kRt*), and rw the
+    // route weights
+    const uint8_t *W2;
+    const int32_t *rt;
+    const double *logits;
+    int32_t *sel, *sel_out;
+    float *rw, *w_out;
+    float *act;
+    int32_t E, F, K, tpe;  // experts, expert rows, routes per token, 16-row tiles per expert
 };
 
 // Operand planes per image: MODE 0 one (hi and lo packed), 1 two (hi, lo),
@@ -79,11 +95,63 @@ __host__ __device__ constexpr size_t ws_lds_bytes(uint32_t slot) {
     return 2 * KS * (size_t)Mode<MODE>::IMG_U32 * 4 + (size_t)kWaves * kTileRows * slot;
 }
 
-template <class F, int MODE, bool RA, int UNITS, int KS = 1>
+// MOE: the tiles are the gate and up rows of the distinct experts in the
+// route table, in pairs (wave 2i a gate tile, wave 2i + 1 the up tile of the
+// same 16 rows), and the epilogue forms the SwiGLU activations of every
+// token that chose the expert instead of storing Y.
+template <class F, int MODE, bool RA, int UNITS, int KS = 1, bool MOE = false>
 __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
     using M = Mode<MODE, KS>;
     static_assert(KS == 1 || KS == 2, "one or two column ranges per workgroup");
+    static_assert(!MOE || (KS == 1 && MODE == 0), "MoE tokens: batch <= 8, one range");
     constexpr int TPG = kWaves / KS;  // tiles per workgroup
+    // MOE: every workgroup routes the T tokens (wave t routes token t, as
+    // the single-token chain does), and one wave lists the distinct experts
+    // in route order with each one's slot per token; workgroup 0 publishes
+    // the routes for the down kernel
+    __shared__ int s_sel[MOE ? kMaxRoutes : 1];
+    __shared__ float s_rw[MOE ? kMaxRoutes : 1];
+    __shared__ RouteLds s_rl[MOE ? kWaves : 1];
+    __shared__ int s_uexp[MOE ? kMaxRoutes : 1];
+    __shared__ int s_uslot[MOE ? kMaxRoutes : 1][kMaxTokens];
+    __shared__ int s_nu;
+    int nu = 0;
+    if constexpr (MOE) {
+        static_assert(kMaxRoutes == 64 && kMaxTokens == 8, "route table layout");
+        const int tid0 = threadIdx.x, w0 = tid0 >> 6;
+        if (p.rt) {
+            // routed already: the table and the weights into LDS
+            for (int i = tid0; i < kMaxRoutes; i += kThreads) s_uexp[i] = p.rt[i];
+            for (int i = tid0; i < kMaxRoutes * kMaxTokens; i += kThreads)
+                (&s_uslot[0][0])[i] = p.rt[kRtSlot + i];
+            for (int i = tid0; i < p.batch * p.K; i += kThreads) s_rw[i] = p.rw[i];
+            if (tid0 == 0) s_nu = p.rt[kRtCount];
+            __syncthreads();
+            nu = s_nu;
+            if ((int64_t)blockIdx.x * (TPG / 2) >= (int64_t)nu * p.tpe) return;
+        } else {
+            for (int i = tid0; i < kMaxRoutes * kMaxTokens; i += kThreads) (&s_uslot[0][0])[i] = -1;
+            __syncthreads();
+            if (w0 < p.batch)
+                route_topk_wave(p.logits + (int64_t)w0 * p.E, p.E, p.K, s_sel + w0 * p.K,
+                                s_rw + w0 * p.K, &s_rl[w0]);
+            __syncthreads();
+            if (w0 == 0) {
+                const int n = distinct_experts(s_sel, p.batch * p.K, p.K, s_uexp, s_uslot);
+                if ((tid0 & 63) == 0) s_nu = n;
+            }
+            __syncthreads();
+            if (blockIdx.x == 0 && tid0 < p.batch * p.K) {
+                p.sel[tid0] = s_sel[tid0];
+                p.rw[tid0] = s_rw[tid0];
+                if (p.sel_out) p.sel_out[tid0] = s_sel[tid0];
+                if (p.w_out) p.w_out[tid0] = s_rw[tid0];
+            }
+            // workgroups past the distinct experts' tiles have nothing more to do
+            nu = s_nu;
+            if ((int64_t)blockIdx.x * (TPG / 2) >= (int64_t)nu * p.tpe) return;
+        }
+    }
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -93,8 +161,15 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
     const int r = lane & 15, q = lane >> 4;
     const int group = (int)(blockIdx.x / (uint32_t)p.kg);
     const int kgi = (int)(blockIdx.x % (uint32_t)p.kg);
-    const int64_t tile = (int64_t)group * TPG + wave % TPG;
-    const bool has_tile = tile < p.tiles;
+    int64_t tile = (int64_t)group * TPG + wave % TPG;
+    bool has_tile = tile < p.tiles;
+    int moe_u = 0, moe_j = 0;
+    if constexpr (MOE) {
+        const int pair = (int)blockIdx.x * (TPG / 2) + wave / 2;
+        moe_u = pair / p.tpe;
+        moe_j = pair - moe_u * p.tpe;
+        has_tile = moe_u < nu;
+    }
     // column range kgi * KS + half of kg * KS; every range of the workgroup
     // runs the same number of steps (the longest range's), so that the
     // barriers match
@@ -172,8 +247,13 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
     };
 
     // ---- weights: the wave's tile, staged chunk by chunk into its slot
-    const uint64_t tb = (uint64_t)(has_tile ? tile : 0) * kTileRows * p.row_bytes;
+    uint64_t tb = (uint64_t)(has_tile ? tile : 0) * kTileRows * p.row_bytes;
     const uint8_t *gp = p.W + tb;
+    if constexpr (MOE) {
+        const uint32_t e = has_tile ? (uint32_t)s_uexp[moe_u] : 0u;
+        tb = ((uint64_t)e * p.F + (uint64_t)moe_j * kTileRows) * p.row_bytes;
+        gp = ((wave & 1) ? p.W2 : p.W) + tb;
+    }
     const uint8_t *al = (const uint8_t *)((uintptr_t)gp & ~(uintptr_t)15);
     const uint32_t d0 = (uint32_t)(gp - al);
     const uint64_t rem = (p.w_bytes - tb + d0 + 15) & ~(uint64_t)15;
@@ -354,6 +434,28 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
 #pragma unroll
             for (int i = 0; i < 4; i++) acc[j][i] += o[i];
         }
+    }
+    if constexpr (MOE) {
+        // the up tile's sums go to the gate tile's wave through LDS (the
+        // images are free after the last step's barrier), which forms
+        // w * silu(g) * u for each token that chose the expert
+        f32x4 *xch = (f32x4 *)smem + (wave / 2) * 64 + lane;
+        if (wave & 1) xch[0] = acc[0];
+        __syncthreads();
+        if ((wave & 1) || !has_tile || q >= 2) return;
+        const f32x4 up = xch[0];
+        const int row = moe_j * kTileRows + r;
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int b = 4 * q + i;
+            const int sl = b < p.batch ? s_uslot[moe_u][b] : -1;
+            if (sl >= 0) {
+                const float g = acc[0][i];
+                p.act[((int64_t)b * p.K + sl) * p.F + row] =
+                    s_rw[b * p.K + sl] * (g / (1.0f + expf(-g))) * up[i];
+            }
+        }
+        return;
     }
     const int64_t row = tile * kTileRows + r;
     if (has_tile && row < p.rows && (MODE != 0 || q < 2)) {

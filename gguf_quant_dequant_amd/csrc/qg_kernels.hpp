@@ -832,6 +832,10 @@ __global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
 // One wave; lane i holds route i (T*K <= 64).
 constexpr int kMaxTokens = 8;
 constexpr int kMaxRoutes = 64;
+// The route table of several tokens, in int32 words: the distinct experts
+// in route order (kMaxRoutes), each one's slot for each token (-1: none,
+// kMaxRoutes x kMaxTokens from kRtSlot), their count (at kRtCount).
+constexpr int kRtSlot = kMaxRoutes, kRtCount = kMaxRoutes * (1 + kMaxTokens);
 
 __device__ __forceinline__ int distinct_experts(const int *s_sel, int nroutes, int K,
                                                 int *s_uexp, int (*s_uslot)[kMaxTokens]) {

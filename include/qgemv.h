@@ -317,11 +317,14 @@ size_t moe_ffn_tokens_workspace_bytes(int64_t tokens, int64_t n_experts,
  *   y[t] = residual[t] + sum_s down[e_{t,s}] a[t][s]   for t < T,
  *
  * with every quantity as moe_ffn defines it for token t.  The expert GEMVs
- * are grouped by expert: within each group of up to four tokens, the gate
- * and up rows of every expert that a token of the group selected are read
- * once and dotted with the group's activations (weight_matrix.rs
- * apply_batch semantics), and each token that chose the expert receives
- * its own SwiGLU activation.  The down GEMVs run per token.
+ * are grouped by expert: the gate and up rows of every expert that any of
+ * the T tokens selected are read once per call and dotted with all T
+ * tokens' activations (weight_matrix.rs apply_batch semantics) on the
+ * matrix cores, as qgemv does at batch 2..8 (bf16 codes, each activation
+ * split into bf16 hi + lo parts, f32 sums; an expert_dim that is not a
+ * multiple of 16 takes the vector ALUs in groups of up to four tokens), and
+ * each token that chose the expert receives its own SwiGLU activation.
+ * The down GEMVs run per token.
  *
  *   x, residual, y  float [T][H]; y may alias residual, not x.
  *   tokens       T, 1..8, with T * top_k <= 64.
@@ -330,8 +333,8 @@ size_t moe_ffn_tokens_workspace_bytes(int64_t tokens, int64_t n_experts,
  *                aligned; its first T * E doubles hold the logits [T][E].
  *   Other arguments as moe_ffn.  T = 1 runs the moe_ffn kernels.
  *   Results per token equal moe_ffn's on that token to the moe_ffn
- *   tolerance (the expert dot products are summed with the batch-B tile
- *   widths, a different order); the routing is identical.
+ *   tolerance (the gate and up dot products are formed as above, in a
+ *   different order); the routing is identical.
  */
 int moe_ffn_tokens(const float *x, const float *residual, float *y,
                    const float *router, int gate_fmt, const void *gate,
