@@ -162,13 +162,6 @@ int moe_ffn_impl(const char *who, const float *x, const float *residual, float *
         return fail(QG_EUNSUPPORTED, "%s: sizes do not tile", who);
     if (hidden / moe_cpt(gate_fmt) > 512 || top_k * (expert_dim / moe_cpt(down_fmt)) > 512)
         return fail(QG_EUNSUPPORTED, "%s: hidden or top_k * expert_dim too large", who);
-    // several tokens: the gate/up tiles are the batch-4 GEMV's
-    if (tokens > 1) {
-        const int cpt4 = gemv_cpt(gate_fmt, 4, hidden);
-        if (cpt4 == 0 || hidden % cpt4 != 0 || hidden / cpt4 > 512)
-            return fail(QG_EUNSUPPORTED, "%s: hidden %lld too wide for several tokens", who,
-                        (long long)hidden);
-    }
 
     uint8_t *ws = (uint8_t *)workspace;
     MoeParams p{};
@@ -219,11 +212,8 @@ int moe_ffn_impl(const char *who, const float *x, const float *residual, float *
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return fail(QG_ELAUNCH, "%s: router launch failed: %s", who,
                                      hipGetErrorString(e));
-#ifndef QG_MOE_TOKENS_MX
-#define QG_MOE_TOKENS_MX 1
-#endif
     int rc;
-    if (tokens > 1 && QG_MOE_TOKENS_MX && expert_dim % 16 == 0) {
+    if (tokens > 1) {
         // several tokens: the distinct experts' gate and up rows on the
         // matrix cores with the tokens as the batch (each row read once per
         // call).  Up to four tokens every gate/up workgroup routes them; above
@@ -245,8 +235,7 @@ int moe_ffn_impl(const char *who, const float *x, const float *residual, float *
                            p.E, p.x, p.logits, rt, p.ws_sel, p.ws_w, sel_experts, sel_weights,
                            p.act, st);
     } else {
-        rc = tokens > 1 ? dispatch_gateup_tokens(gate_fmt, p, st)
-                        : (q8 ? dispatch_gateup_q8(gate_fmt, p, st) : dispatch_gateup(gate_fmt, p, st));
+        rc = q8 ? dispatch_gateup_q8(gate_fmt, p, st) : dispatch_gateup(gate_fmt, p, st);
     }
     if (rc != QG_OK) return rc;
     rc = q8 ? dispatch_down_q8(down_fmt, p, st) : dispatch_down(down_fmt, p, st);

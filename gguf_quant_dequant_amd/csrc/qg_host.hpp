@@ -286,7 +286,6 @@ template <int NB>
 int gemm_b(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
            int batch, int64_t rb, hipStream_t st);
 int dispatch_gateup(int fmt, const MoeParams &p, hipStream_t st);
-int dispatch_gateup_tokens(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_down(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_gateup_q8(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_down_q8(int fmt, const MoeParams &p, hipStream_t st);

@@ -855,138 +855,6 @@ __device__ __forceinline__ int distinct_experts(const int *s_sel, int nroutes, i
     return __popcll(m);
 }
 
-// Routing of the group's T tokens (wave w routes tokens w, w + waves, ...),
-// the distinct-expert table, then row tasks (distinct expert u, row j): the
-// gate and up rows of expert s_uexp[u] are read once and dotted with the B
-// activation vectors (tokens past T are zero), and every token t that chose
-// the expert in slot s gets act[t][s][j] = w[t][s] * silu(g_t) * u_t.
-template <class F, int B, int U>
-__global__ void __launch_bounds__(512) moe_gateup_tokens_kernel(MoeParams p) {
-    __shared__ int s_sel[kMaxRoutes];
-    __shared__ RouteLds s_rt[8];  // one per wave (blockDim <= 512)
-    __shared__ float s_w[kMaxRoutes];
-    __shared__ int s_uexp[kMaxRoutes];
-    __shared__ int s_uslot[kMaxRoutes][kMaxTokens];
-    __shared__ int s_nu;
-    __shared__ float red[8][2 * U * B];
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    int grp, lig;
-    if (p.gu_S == 1) {
-        grp = wave * (64 / p.gu_lpr) + lane / p.gu_lpr;
-        lig = lane & (p.gu_lpr - 1);
-    } else {
-        grp = wave / p.gu_S;
-        lig = (wave % p.gu_S) * 64 + lane;
-    }
-    const bool active = lig < p.gu_tiles;
-    const typename F::Lane L = F::init(active ? lig : 0);
-    const int T = p.T, K = p.K;
-    for (int i = tid; i < kMaxRoutes * kMaxTokens; i += blockDim.x) (&s_uslot[0][0])[i] = -1;
-    // the T activation vectors are staged through LDS while the waves route
-    // (wave w takes tokens w, w + waves, ...); the staging's barriers
-    // publish the routes
-    extern __shared__ __attribute__((aligned(16))) uint32_t xst[];
-    const uint32_t nthr = blockDim.x, xcap = 32u * nthr, H = (uint32_t)p.H;
-    const uint32_t xtot = (uint32_t)T * H;
-    const rsrc_t rx = make_rsrc(p.x, 4u * xtot);
-    uint32_t xr[kStageChunks][4];
-    xs_fetch(rx, 0u, (xtot < xcap ? xtot : xcap) / 4u, tid, nthr, xr);
-    for (int t = wave; t < T; t += (int)(blockDim.x >> 6))
-        route_topk_wave(p.logits + (int64_t)t * p.E, p.E, K, s_sel + t * K, s_w + t * K,
-                        &s_rt[wave]);
-    typename F::template XTile<B> xt;
-    {
-        uint32_t xbase[B];
-#pragma unroll
-        for (int b = 0; b < B; b++) xbase[b] = (uint32_t)b * H;  // b >= T: past X, stays 0
-        float x[B][F::CPT];
-        xs_stage<F, B>(xst, rx, xtot, xbase, L, active, tid, nthr, xr, x);
-        F::template prep<B>(x, xt);
-    }
-    if (wave == 0) {
-        const int nu = distinct_experts(s_sel, T * K, K, s_uexp, s_uslot);
-        if (lane == 0) s_nu = nu;
-    }
-    if (blockIdx.x == 0 && tid < T * K) {
-        p.ws_sel[tid] = s_sel[tid];
-        p.ws_w[tid] = s_w[tid];
-        if (p.sel_out) p.sel_out[tid] = s_sel[tid];
-        if (p.w_out) p.w_out[tid] = s_w[tid];
-    }
-    __syncthreads();
-
-    uint32_t dg, du;
-    const rsrc_t rg = rows_rsrc(p.gate, p.gate_bytes, 0, &dg);
-    const rsrc_t ru = rows_rsrc(p.up, p.up_bytes, 0, &du);
-    const int64_t tasks = (int64_t)s_nu * p.F;
-    const int64_t tpi = (int64_t)p.gu_G * U;
-    for (int64_t it = blockIdx.x; it * tpi < tasks; it += gridDim.x) {
-        const int64_t t0 = it * tpi + (int64_t)grp * U;
-        typename F::Raw rawg[U], rawu[U];
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            const int64_t t = t0 + u;
-            const bool want = active && t < tasks;
-            const int ue = want ? (int)(t / p.F) : 0, j = want ? (int)(t % p.F) : 0;
-            const uint32_t off = ((uint32_t)s_uexp[ue] * (uint32_t)p.F + (uint32_t)j) * p.rb_gate;
-            F::load(BufReader{rg}, want ? dg + off : kOorRow, L, rawg[u]);
-            F::load(BufReader{ru}, want ? du + off : kOorRow, L, rawu[u]);
-        }
-        float v[2 * U * B];
-#pragma unroll
-        for (int u = 0; u < U; u++) {
-            float ag[B], au[B];
-#pragma unroll
-            for (int b = 0; b < B; b++) ag[b] = au[b] = 0.f;
-            if (active && t0 + u < tasks) {
-                F::template dot<B>(rawg[u], L, xt, ag);
-                F::template dot<B>(rawu[u], L, xt, au);
-            }
-#pragma unroll
-            for (int b = 0; b < B; b++) {
-                v[(2 * u) * B + b] = ag[b];
-                v[(2 * u + 1) * B + b] = au[b];
-            }
-        }
-        group_sum_all(v, p.gu_S == 1 ? p.gu_lpr : 64);
-        if (p.gu_S != 1) {
-            // the S waves of a group add their partial sums in wave order
-            if (lane == 0) {
-#pragma unroll
-                for (int i = 0; i < 2 * U * B; i++) red[wave][i] = v[i];
-            }
-            __syncthreads();
-            if (wave % p.gu_S == 0) {
-#pragma unroll
-                for (int i = 0; i < 2 * U * B; i++) {
-                    float a = 0.f;
-                    for (int w = 0; w < p.gu_S; w++) a += red[wave + w][i];
-                    v[i] = a;
-                }
-            }
-        }
-        const bool writer = p.gu_S == 1 ? lig == 0 : (wave % p.gu_S == 0 && lane == 0);
-        if (writer) {
-#pragma unroll
-            for (int u = 0; u < U; u++) {
-                const int64_t t = t0 + u;
-                if (t < tasks) {
-                    const int ue = (int)(t / p.F), j = (int)(t % p.F);
-#pragma unroll
-                    for (int b = 0; b < B; b++) {
-                        const int s = b < T ? s_uslot[ue][b] : -1;
-                        if (s >= 0)
-                            p.act[((int64_t)b * K + s) * p.F + j] =
-                                s_w[b * K + s] * silu_f(v[(2 * u) * B + b]) *
-                                v[(2 * u + 1) * B + b];
-                    }
-                }
-            }
-        }
-        if (p.gu_S != 1) __syncthreads();
-    }
-}
-
 // ------------------------------------------------------------------ MoE K3
 
 template <class F, int U>

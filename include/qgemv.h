@@ -322,9 +322,8 @@ size_t moe_ffn_tokens_workspace_bytes(int64_t tokens, int64_t n_experts,
  * the T tokens selected are read once per call and dotted with all T
  * tokens' activations (weight_matrix.rs apply_batch semantics) on the
  * matrix cores, as qgemv does at batch 2..8 (bf16 codes, each activation
- * split into bf16 hi + lo parts, f32 sums; an expert_dim that is not a
- * multiple of 16 takes the vector ALUs in groups of up to four tokens), and
- * each token that chose the expert receives its own SwiGLU activation.
+ * split into bf16 hi + lo parts, f32 sums), and each token that chose the
+ * expert receives its own SwiGLU activation.
  * The down GEMVs run per token.
  *
  *   x, residual, y  float [T][H]; y may alias residual, not x.

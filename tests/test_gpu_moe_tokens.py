@@ -162,3 +162,20 @@ def test_non_finite_token_does_not_reach_other_tokens_logits():
     assert np.all(np.abs(logits[0] - r["logits"]) <= 1e-12 * lb)
     assert np.array_equal(sel[0], r["sel"])
     assert_agree(y[0], r["y"], r["bound"], "token 0 beside a non-finite token")
+
+
+@pytest.mark.parametrize("T", [3, 6])
+def test_hidden_of_32768_columns(T):
+    # the widest hidden the chain takes (512 lane tiles of the single-token
+    # kernels): 128 chunks of 256 columns per gate / up row, Q8_0 down rows
+    # of 64 columns
+    E, k, H, F = 4, 2, 32768, 64
+    g = synth.rng(71 + T)
+    router = synth.f32_matrix(g, E, H, 0.02)
+    gate = synth.matrix(g, q.QG_Q4_K, E * F, H)
+    up = synth.matrix(g, q.QG_Q4_K, E * F, H)
+    down = synth.matrix(g, q.QG_Q8_0, E * H, F)
+    m = MoeTokens(router, gate, up, down, q.QG_Q4_K, q.QG_Q8_0, E, k, H, F)
+    x = synth.activations(g, T, H)
+    res = synth.activations(g, T, H)
+    _compare(m, x, res, f"hidden 32768, {T} tokens")
