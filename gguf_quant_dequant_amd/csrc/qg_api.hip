@@ -218,21 +218,20 @@ int moe_ffn_impl(const char *who, const float *x, const float *residual, float *
         // matrix cores with the tokens as the batch (each row read once per
         // call).  Up to four tokens every gate/up workgroup routes them; above
         // that the grid outnumbers the workgroups the device holds at once,
-        // and one small kernel routes ahead (4 tokens: 53.0 -> 50.9 us per
-        // call routing in the workgroups; 8 tokens: 81.2 -> 87.6 us).
-        const int32_t *rt = nullptr;
-        if (tokens > 4) {
-            int32_t *rtw = (int32_t *)(ws + wl.rt);
-            hipLaunchKernelGGL(moe_route_tokens_kernel, dim3(1), dim3(512), 0, st,
+        // and a small kernel of one wave per token routes ahead (per call,
+        // routed in the workgroups / ahead: 4 tokens 48.4 / 50.0 us, 8 tokens
+        // 76.5 / 74.9 us).
+        const bool routed = tokens > 4;
+        if (routed) {
+            hipLaunchKernelGGL(moe_route_tokens_kernel, dim3((unsigned)tokens), dim3(64), 0, st,
                                (const double *)(ws + wl.logits), (int)n_experts, (int)top_k,
-                               (int)tokens, p.ws_sel, p.ws_w, sel_experts, sel_weights, rtw);
+                               p.ws_sel, p.ws_w, sel_experts, sel_weights);
             e = hipGetLastError();
             if (e != hipSuccess) return fail(QG_ELAUNCH, "%s: routing launch failed: %s", who,
                                              hipGetErrorString(e));
-            rt = rtw;
         }
         rc = moe_gateup_ws(gate_fmt, p.gate, p.up, p.gate_bytes, p.rb_gate, p.H, p.F, p.K, p.T,
-                           p.E, p.x, p.logits, rt, p.ws_sel, p.ws_w, sel_experts, sel_weights,
+                           p.E, p.x, p.logits, routed, p.ws_sel, p.ws_w, sel_experts, sel_weights,
                            p.act, st);
     } else {
         rc = q8 ? dispatch_gateup_q8(gate_fmt, p, st) : dispatch_gateup(gate_fmt, p, st);

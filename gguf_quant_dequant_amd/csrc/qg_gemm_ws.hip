@@ -150,13 +150,13 @@ int gemm_ks2(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
 }
 
 // The gate and up products of T <= 8 MoE tokens on the shared-activation
-// kernel: every workgroup routes the tokens (or, with rt, reads the routing
-// done ahead), then takes 4 pairs of gate / up tiles of the distinct experts
+// kernel: every workgroup routes the tokens (or, when routed, reads the
+// routes done ahead), then takes 4 pairs of gate / up tiles of the distinct experts
 // (at most T * K of them) with SwiGLU in the epilogue.
 template <class F>
 int launch_moe_ws(const uint8_t *gate, const uint8_t *up, uint64_t stack_bytes, int64_t rb,
                   int H, int F_, int K, int T, int E, const float *x, const double *logits,
-                  const int32_t *rt, int32_t *sel, float *rw, int32_t *sel_out, float *w_out,
+                  bool routed, int32_t *sel, float *rw, int32_t *sel_out, float *w_out,
                   float *act, hipStream_t st) {
     gw::WsParams p{};
     p.W = gate;
@@ -172,7 +172,7 @@ int launch_moe_ws(const uint8_t *gate, const uint8_t *up, uint64_t stack_bytes, 
     p.nu = gemm_nu(F::CHUNK);
     p.slot = 16u * (uint32_t)(p.nu | 1);
     p.logits = logits;
-    p.rt = rt;
+    p.routed = routed ? 1 : 0;
     p.sel = sel;
     p.rw = rw;
     p.sel_out = sel_out;
@@ -191,7 +191,8 @@ int launch_moe_ws(const uint8_t *gate, const uint8_t *up, uint64_t stack_bytes, 
     constexpr int U = gemm_units(F::CHUNK);
     auto kern = ra ? gw::qgemm_ws_kernel<F, 0, true, U, 1, true>
                    : gw::qgemm_ws_kernel<F, 0, F::CHUNK % 4 != 0, U, 1, true>;
-    const size_t lds = gw::ws_lds_bytes<0, 1>(p.slot);
+    // the dynamic LDS doubles as the routing's E words of scratch
+    const size_t lds = std::max(gw::ws_lds_bytes<0, 1>(p.slot), (size_t)4 * E);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(gw::kThreads), lds, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess)
@@ -201,10 +202,10 @@ int launch_moe_ws(const uint8_t *gate, const uint8_t *up, uint64_t stack_bytes, 
 
 int moe_gateup_ws(int fmt, const uint8_t *gate, const uint8_t *up, uint64_t stack_bytes,
                   int64_t rb, int H, int F, int K, int T, int E, const float *x,
-                  const double *logits, const int32_t *rt, int32_t *sel, float *rw,
+                  const double *logits, bool routed, int32_t *sel, float *rw,
                   int32_t *sel_out, float *w_out, float *act, hipStream_t st) {
 #define QG_MOE_WS_CASE(FM)                                                                   \
-    return launch_moe_ws<FM>(gate, up, stack_bytes, rb, H, F, K, T, E, x, logits, rt, sel,   \
+    return launch_moe_ws<FM>(gate, up, stack_bytes, rb, H, F, K, T, E, x, logits, routed, sel,   \
                              rw, sel_out, w_out, act, st)
     switch (fmt) {
     case QG_Q4_K: QG_MOE_WS_CASE(gm::GK45<false>);

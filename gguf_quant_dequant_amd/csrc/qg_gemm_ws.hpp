@@ -59,12 +59,10 @@ struct WsParams {
     // the gate stack, W2 the up stack (w_bytes each), X the T = batch tokens'
     // activations, logits their router logits [T][E]; the routes and route
     // weights [T][K] are written to sel and rw (and sel_out, w_out when
-    // given), the SwiGLU activations [T][K][F] to act.  With rt set the
-    // routing has been done (moe_route_tokens_kernel): rt holds the distinct
-    // experts, their slots per token and their count (kRt*), and rw the
-    // route weights
+    // given), the SwiGLU activations [T][K][F] to act.  With routed set the
+    // routing has been done (moe_route_tokens_kernel) and sel and rw hold it
     const uint8_t *W2;
-    const int32_t *rt;
+    int32_t routed;
     const double *logits;
     int32_t *sel, *sel_out;
     float *rw, *w_out;
@@ -95,8 +93,8 @@ __host__ __device__ constexpr size_t ws_lds_bytes(uint32_t slot) {
     return 2 * KS * (size_t)Mode<MODE>::IMG_U32 * 4 + (size_t)kWaves * kTileRows * slot;
 }
 
-// MOE: the tiles are the gate and up rows of the distinct experts in the
-// route table, in pairs (wave 2i a gate tile, wave 2i + 1 the up tile of the
+// MOE: the tiles are the gate and up rows of the tokens' distinct experts,
+// in pairs (wave 2i a gate tile, wave 2i + 1 the up tile of the
 // same 16 rows), and the epilogue forms the SwiGLU activations of every
 // token that chose the expert instead of storing Y.
 template <class F, int MODE, bool RA, int UNITS, int KS = 1, bool MOE = false>
@@ -106,9 +104,10 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
     static_assert(!MOE || (KS == 1 && MODE == 0), "MoE tokens: batch <= 8, one range");
     constexpr int TPG = kWaves / KS;  // tiles per workgroup
     // MOE: every workgroup routes the T tokens (wave t routes token t, as
-    // the single-token chain does), and one wave lists the distinct experts
-    // in route order with each one's slot per token; workgroup 0 publishes
-    // the routes for the down kernel
+    // the single-token chain does; workgroup 0 publishes the routes for the
+    // down kernel) or, when routed ahead, reads their routes, and one wave
+    // lists the distinct experts in route order with each one's slot per
+    // token
     __shared__ int s_sel[MOE ? kMaxRoutes : 1];
     __shared__ float s_rw[MOE ? kMaxRoutes : 1];
     __shared__ RouteLds s_rl[MOE ? kWaves : 1];
@@ -117,29 +116,20 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
     __shared__ int s_nu;
     int nu = 0;
     if constexpr (MOE) {
-        static_assert(kMaxRoutes == 64 && kMaxTokens == 8, "route table layout");
         const int tid0 = threadIdx.x, w0 = tid0 >> 6;
-        if (p.rt) {
-            // routed already: the table and the weights into LDS
-            for (int i = tid0; i < kMaxRoutes; i += kThreads) s_uexp[i] = p.rt[i];
-            for (int i = tid0; i < kMaxRoutes * kMaxTokens; i += kThreads)
-                (&s_uslot[0][0])[i] = p.rt[kRtSlot + i];
-            for (int i = tid0; i < p.batch * p.K; i += kThreads) s_rw[i] = p.rw[i];
-            if (tid0 == 0) s_nu = p.rt[kRtCount];
+        for (int i = tid0; i < kMaxRoutes * kMaxTokens; i += kThreads) (&s_uslot[0][0])[i] = -1;
+        if (p.routed) {
+            // routed ahead (one workgroup per token): the routes and weights
+            for (int i = tid0; i < p.batch * p.K; i += kThreads) {
+                s_sel[i] = p.sel[i];
+                s_rw[i] = p.rw[i];
+            }
             __syncthreads();
-            nu = s_nu;
-            if ((int64_t)blockIdx.x * (TPG / 2) >= (int64_t)nu * p.tpe) return;
         } else {
-            for (int i = tid0; i < kMaxRoutes * kMaxTokens; i += kThreads) (&s_uslot[0][0])[i] = -1;
             __syncthreads();
             if (w0 < p.batch)
                 route_topk_wave(p.logits + (int64_t)w0 * p.E, p.E, p.K, s_sel + w0 * p.K,
                                 s_rw + w0 * p.K, &s_rl[w0]);
-            __syncthreads();
-            if (w0 == 0) {
-                const int n = distinct_experts(s_sel, p.batch * p.K, p.K, s_uexp, s_uslot);
-                if ((tid0 & 63) == 0) s_nu = n;
-            }
             __syncthreads();
             if (blockIdx.x == 0 && tid0 < p.batch * p.K) {
                 p.sel[tid0] = s_sel[tid0];
@@ -147,10 +137,18 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
                 if (p.sel_out) p.sel_out[tid0] = s_sel[tid0];
                 if (p.w_out) p.w_out[tid0] = s_rw[tid0];
             }
-            // workgroups past the distinct experts' tiles have nothing more to do
-            nu = s_nu;
-            if ((int64_t)blockIdx.x * (TPG / 2) >= (int64_t)nu * p.tpe) return;
         }
+        if (w0 == 0) {
+            // the dynamic LDS is free until the main loop: the experts' first routes
+            extern __shared__ __attribute__((aligned(16))) int s_dyn[];
+            const int n =
+                distinct_experts(s_sel, p.batch * p.K, p.K, p.E, s_dyn, s_uexp, s_uslot);
+            if ((tid0 & 63) == 0) s_nu = n;
+        }
+        __syncthreads();
+        // workgroups past the distinct experts' tiles have nothing more to do
+        nu = s_nu;
+        if ((int64_t)blockIdx.x * (TPG / 2) >= (int64_t)nu * p.tpe) return;
     }
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int tid = threadIdx.x, lane = tid & 63;

@@ -244,22 +244,18 @@ inline bool tiles_fit(int fmt, int B, int64_t cols) {
 inline size_t align16(size_t v) { return (v + 15) & ~(size_t)15; }
 
 struct WsLayout {
-    size_t logits, sel, w, act, rt, total;
+    size_t logits, sel, w, act, total;
 };
 
 // Sections for T tokens: f64 logits [T][E], int32 routes [T][K], f32
-// weights [T][K], f32 activations [T][K][F], for T > 1 the route table of
-// their distinct experts, each 16-byte aligned.
+// weights [T][K], f32 activations [T][K][F], each 16-byte aligned.
 inline WsLayout ws_layout(int64_t E, int64_t K, int64_t F, int64_t T = 1) {
     WsLayout l;
     l.logits = 0;
     l.sel = align16(8 * (size_t)(T * E));
     l.w = l.sel + align16(4 * (size_t)(T * K));
     l.act = l.w + align16(4 * (size_t)(T * K));
-    l.rt = l.act + align16(4 * (size_t)(T * K) * (size_t)F);
-    // several tokens: the route table of their distinct experts (64
-    // experts, 64 x 8 slots, the count, in int32 words)
-    l.total = l.rt + (T > 1 ? align16(4 * (size_t)(64 * 9 + 4)) : 0);
+    l.total = l.act + align16(4 * (size_t)(T * K) * (size_t)F);
     return l;
 }
 
@@ -294,7 +290,7 @@ int ws_kg(int64_t rows, int64_t cols, int batch);
 bool gemm_ks2_fits(int fmt, int64_t rows, int64_t cols, int batch);
 int moe_gateup_ws(int fmt, const uint8_t *gate, const uint8_t *up, uint64_t stack_bytes,
                   int64_t rb, int H, int F, int K, int T, int E, const float *x,
-                  const double *logits, const int32_t *rt, int32_t *sel, float *rw,
+                  const double *logits, bool routed, int32_t *sel, float *rw,
                   int32_t *sel_out, float *w_out, float *act, hipStream_t st);
 int gemm_ks2(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
              int batch, int64_t rb, hipStream_t st);

@@ -829,23 +829,20 @@ __global__ void __launch_bounds__(512) moe_gateup_kernel(MoeParams p) {
 
 // The distinct experts among the T*K routes, in route order (token-major,
 // then rank), and for each the slot every token holds it in (-1: none).
-// One wave; lane i holds route i (T*K <= 64).
+// One wave; lane i holds route i (T*K <= 64).  s_first is LDS scratch of E
+// words: the lowest route index of each expert, found with one LDS minimum
+// per route (the LDS operations of one wave take effect in program order).
 constexpr int kMaxTokens = 8;
 constexpr int kMaxRoutes = 64;
-// The route table of several tokens, in int32 words: the distinct experts
-// in route order (kMaxRoutes), each one's slot for each token (-1: none,
-// kMaxRoutes x kMaxTokens from kRtSlot), their count (at kRtCount).
-constexpr int kRtSlot = kMaxRoutes, kRtCount = kMaxRoutes * (1 + kMaxTokens);
 
-__device__ __forceinline__ int distinct_experts(const int *s_sel, int nroutes, int K,
-                                                int *s_uexp, int (*s_uslot)[kMaxTokens]) {
+__device__ __forceinline__ int distinct_experts(const int *s_sel, int nroutes, int K, int E,
+                                                int *s_first, int *s_uexp,
+                                                int (*s_uslot)[kMaxTokens]) {
     const int lane = __lane_id();
-    const int e = lane < nroutes ? s_sel[lane] : -1 - lane;
-    int first = lane;  // lowest route index holding the same expert
-    for (int j = nroutes - 1; j >= 0; j--) {
-        const int ej = __shfl(e, j);
-        if (ej == e && j < lane) first = j;
-    }
+    for (int i = lane; i < E; i += 64) s_first[i] = 64;
+    const int e = lane < nroutes ? s_sel[lane] : -1;
+    if (e >= 0) atomicMin(&s_first[e], lane);
+    const int first = e >= 0 ? s_first[e] : lane;  // lowest route index holding e
     const bool lead = lane < nroutes && first == lane;
     const unsigned long long m = __ballot(lead);
     const int u_lead = __popcll(m & ((1ull << lane) - 1ull));

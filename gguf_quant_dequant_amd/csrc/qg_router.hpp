@@ -16,44 +16,26 @@ __global__ void __launch_bounds__(64) route_topk_kernel(const double *logits, in
 // The routing of T tokens ahead of the grouped gate/up products on the
 // matrix cores, once for all their workgroups (at more than four tokens the
 // workgroups outnumber what the device holds at once, and routing in each
-// of them would repeat it): one workgroup, wave w routes tokens w, w + 8, ...
-// (the single-token routing, bit for bit), then one wave lists the distinct
-// experts in route order with each one's slot per token.  Writes the routes
-// and weights of every token (workspace and optional outputs) and the table
-// the gate/up workgroups read (kRtSlot, kRtCount).
-__global__ void __launch_bounds__(512) moe_route_tokens_kernel(const double *logits, int E, int K,
-                                                               int T, int *sel, float *w,
-                                                               int *sel_out, float *w_out,
-                                                               int *rt) {
-    static_assert(kMaxRoutes == 64 && kMaxTokens == 8, "route table layout");
-    __shared__ int s_sel[kMaxRoutes];
-    __shared__ float s_w[kMaxRoutes];
-    __shared__ RouteLds s_rt[8];
-    __shared__ int s_uexp[kMaxRoutes];
-    __shared__ int s_uslot[kMaxRoutes][kMaxTokens];
-    __shared__ int s_nu;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    for (int i = tid; i < kMaxRoutes * kMaxTokens; i += blockDim.x) (&s_uslot[0][0])[i] = -1;
-    for (int i = tid; i < kMaxRoutes; i += blockDim.x) s_uexp[i] = 0;
+// of them would repeat it): workgroup t, one wave, routes token t (the
+// single-token routing, bit for bit) and writes its routes and weights to
+// the workspace and the optional outputs.
+__global__ void __launch_bounds__(64) moe_route_tokens_kernel(const double *logits, int E, int K,
+                                                              int *sel, float *w, int *sel_out,
+                                                              float *w_out) {
+    __shared__ RouteLds s_rt;
+    __shared__ int s_sel[kMaxTopK];
+    __shared__ float s_w[kMaxTopK];
+    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x;
+    route_topk_wave(logits + t * E, E, K, s_sel, s_w, &s_rt);
     __syncthreads();
-    for (int t = wave; t < T; t += (int)(blockDim.x >> 6))
-        route_topk_wave(logits + (int64_t)t * E, E, K, s_sel + t * K, s_w + t * K, &s_rt[wave]);
-    __syncthreads();
-    if (wave == 0) {
-        const int nu = distinct_experts(s_sel, T * K, K, s_uexp, s_uslot);
-        if (lane == 0) s_nu = nu;
+    if (lane < K) {
+        const int64_t i = t * K + lane;
+        sel[i] = s_sel[lane];
+        w[i] = s_w[lane];
+        if (sel_out) sel_out[i] = s_sel[lane];
+        if (w_out) w_out[i] = s_w[lane];
     }
-    __syncthreads();
-    for (int i = tid; i < T * K; i += blockDim.x) {
-        sel[i] = s_sel[i];
-        w[i] = s_w[i];
-        if (sel_out) sel_out[i] = s_sel[i];
-        if (w_out) w_out[i] = s_w[i];
-    }
-    for (int i = tid; i < kMaxRoutes; i += blockDim.x) rt[i] = s_uexp[i];
-    for (int i = tid; i < kMaxRoutes * kMaxTokens; i += blockDim.x)
-        rt[kRtSlot + i] = (&s_uslot[0][0])[i];
-    if (tid == 0) rt[kRtCount] = s_nu;
 }
 
 // ------------------------------------------------------------------ MoE K1

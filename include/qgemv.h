@@ -305,9 +305,8 @@ int moe_ffn_noalloc(const float *x, const float *residual, float *y,
                     int32_t *sel_experts, float *sel_weights, void *stream);
 
 /* Bytes of caller-owned device workspace moe_ffn_tokens needs for T tokens
- * (f64 logits [T][E], the routes [T][k], the activations [T][k][F], and for
- * T > 1 the table of their distinct experts, 2320 bytes).  Returns 0 for
- * invalid sizes. */
+ * (f64 logits [T][E], the routes [T][k] and their weights, the activations
+ * [T][k][F], each section 16-byte aligned).  Returns 0 for invalid sizes. */
 size_t moe_ffn_tokens_workspace_bytes(int64_t tokens, int64_t n_experts,
                                       int64_t top_k, int64_t expert_dim);
 

@@ -213,12 +213,12 @@ def test_moe_ffn_tokens_refuses_before_launching(lib, over, code, msg):
 
 
 def test_tokens_workspace_size(lib):
-    # T * E f64 logits, T * k routes and weights, T * k * F activations, and
-    # for T > 1 the route table (580 int32 words), 16-byte sections
+    # T * E f64 logits, T * k routes and weights, T * k * F activations,
+    # 16-byte sections
     assert q.moe_ffn_tokens_workspace_bytes(1, 128, 8, 768) == q.moe_ffn_workspace_bytes(128, 8, 768)
     assert q.moe_ffn_tokens_workspace_bytes(4, 128, 8, 768) == \
-        4 * 128 * 8 + 4 * 8 * 4 + 4 * 8 * 4 + 4 * 8 * 768 * 4 + 2320
-    assert q.moe_ffn_tokens_workspace_bytes(3, 6, 2, 256) == 144 + 32 + 32 + 3 * 2 * 256 * 4 + 2320
+        4 * 128 * 8 + 4 * 8 * 4 + 4 * 8 * 4 + 4 * 8 * 768 * 4
+    assert q.moe_ffn_tokens_workspace_bytes(3, 6, 2, 256) == 144 + 32 + 32 + 3 * 2 * 256 * 4
     assert q.moe_ffn_tokens_workspace_bytes(0, 6, 2, 256) == 0
 
 
