@@ -476,6 +476,9 @@ ARITH = {
                      "activations shared by 4 row tiles, two column ranges added in the workgroup",
     "q8act": "int8 codes x int8 activations (per 16 columns), exact int32 sums, f32 per group",
     "moe": "f64 router, f32 expert GEMVs on the vector ALUs",
+    "moe_tokens": "f64 router, gate/up as bf16 codes x bf16 hi + lo activation parts on the "
+                  "matrix cores (f32 sums, each distinct expert's rows read once per call), "
+                  "down f32 on the vector ALUs",
     "moe_q8": "f64 router, expert GEMVs as int8 codes x int8 activations (per 16 columns), "
               "exact int32 sums, f32 per group",
     "read": "plain read, no arithmetic",
@@ -634,7 +637,7 @@ def main():
                 wall_tokens_per_s=round(steps * T / wall, 1),
                 event_us_per_call=round(per_us, 3),
                 tokens_per_s=round(T * 1e6 / per_us, 1),
-                arith=ARITH["moe"])
+                arith=ARITH["moe_tokens"])
             del m
 
     line = {
