@@ -468,13 +468,24 @@ __global__ void __launch_bounds__(kThreads) qgemm_ws_kernel(WsParams p) {
     }
 }
 
-// Y[b][r] = sum over g < kg of part[g][b][r], in order of g.
+// Y[b][r] = sum over g < kg of part[g][b][r], in order of g.  The partial
+// sums come from other XCDs' caches or memory, so each thread issues eight
+// loads before it adds any of them.
 __global__ void __launch_bounds__(256) ws_reduce_kernel(const float *__restrict__ part,
                                                         float *__restrict__ Y, int64_t n, int kg) {
+    constexpr int G = 8;
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * 256) {
-        float s = part[i];
-        for (int g = 1; g < kg; g++) s += part[(int64_t)g * n + i];
+        float s = 0.f;
+        for (int g0 = 0; g0 < kg; g0 += G) {
+            float v[G];
+#pragma unroll
+            for (int j = 0; j < G; j++)
+                v[j] = g0 + j < kg ? part[(int64_t)(g0 + j) * n + i] : 0.f;
+#pragma unroll
+            for (int j = 0; j < G; j++)
+                if (g0 + j < kg) s = g0 + j == 0 ? v[j] : s + v[j];
+        }
         Y[i] = s;
     }
 }
