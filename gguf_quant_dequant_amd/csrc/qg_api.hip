@@ -51,13 +51,18 @@ __global__ void __launch_bounds__(kStreamThreads) stream_read_kernel(const uint8
 
 // The matrix-core GEMV with the whole row's activation image in LDS
 // (qg_mfma.hpp): batch-1 rows too wide for the VALU kernel, and batch 2..4
-// when the image fits (measured faster there than the batched kernel, e.g.
-// Q5_K 14336 x 4096 at batch 4: 19.9 against 26.7 us).  *done = false when
-// the shape does not fit.
+// on rows of at most 1024 columns, where the batched kernel splits a row
+// over too few waves (at batch 2: Q6_K 4096 x 1024 5.9 us against 8.7,
+// Q4_K 4096 x 1024 5.9 against 7.3).  Wider rows at batch 2..4 are faster
+// on the batched kernels (at batch 2: Q4_K 4096 x 4096 10.9 -> 7.9 us,
+// Q8_0 4096 x 4096 16.7 -> 8.6, Q6_K 4096 x 4096 12.7 -> 9.4, Q4_0 4096 x
+// 14336 84 -> 18.3, Q4_K 2048 x 2048 7.5 -> 7.4; Q5_K 4096 x 4096 at
+// batch 3 12.7 -> 8.3).  *done = false when the shape does not fit.
 int try_mx(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
            int batch, int64_t rb, hipStream_t st, bool *done) {
     *done = false;
     if (fmt == QG_F32 || batch > 4) return QG_OK;
+    if (batch >= 2 && cols > 1024) return QG_OK;
     if (batch == 1) {
         if (tiles_fit(fmt, 1, cols)) return QG_OK;
         return try_mx_b<1>(fmt, W, rows, cols, X, Y, batch, rb, st, done);
@@ -297,19 +302,30 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
     hipStream_t st = (hipStream_t)stream;
     if (const int rc0 = no_pending_error("qgemv")) return rc0;
     bool done = false;
-    if (QG_Q6_MX && fmt == QG_Q6_K && batch == 1) {
-        GemvParams p{};
-        p.W = (const uint8_t *)W;
-        p.X = X;
-        p.Y = Y;
-        p.rows = rows;
-        p.w_bytes = (uint64_t)rows * (uint64_t)rb;
-        p.row_bytes = (uint32_t)rb;
-        p.cols = (uint32_t)cols;
-        p.batch_x = 1;
-        const int qrc = try_q6mx(p, st, &done);
-        if (done) {
+    if (QG_Q6_MX && fmt == QG_Q6_K &&
+        (batch == 1 ||
+         (batch <= QG_Q6_MX_ROWS && (uint64_t)rows * (uint64_t)rb >= QG_Q6_MX_ROWS_BYTES))) {
+        // batch 1, and on matrices of the lm_head's class batch 2 as two
+        // batch-1 launches: the bf16 kernels run Q6_K rows at ~2.2 TB/s
+        // (lm_head 151936 x 2048 at batch 2: 117 us against 2 x 43.5),
+        // the batch-1 kernel reaches its rate only on such sizes (14336 x
+        // 4096 at batch 2: 21.4 us on the bf16 kernel, 34.1 as two launches)
+        for (int b = 0; b < batch; b++) {
+            GemvParams p{};
+            p.W = (const uint8_t *)W;
+            p.X = X + (int64_t)b * cols;
+            p.Y = Y + (int64_t)b * rows;
+            p.rows = rows;
+            p.w_bytes = (uint64_t)rows * (uint64_t)rb;
+            p.row_bytes = (uint32_t)rb;
+            p.cols = (uint32_t)cols;
+            p.batch_x = 1;
+            // the shape decides whether it fits, the same for every row
+            const int qrc = try_q6mx(p, st, &done);
+            if (!done) break;
             if (qrc != QG_OK) return qrc;
+        }
+        if (done) {
             g_kernel = "mfma_i8_q6k";
             return ok();
         }

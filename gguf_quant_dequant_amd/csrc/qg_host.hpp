@@ -63,6 +63,14 @@
 #ifndef QG_Q6_MX
 #define QG_Q6_MX 1
 #endif
+// Batch rows up to which Q6_K runs the batch-1 kernel once per row, on
+// matrices of at least QG_Q6_MX_ROWS_BYTES.
+#ifndef QG_Q6_MX_ROWS
+#define QG_Q6_MX_ROWS 2
+#endif
+#ifndef QG_Q6_MX_ROWS_BYTES
+#define QG_Q6_MX_ROWS_BYTES (128ull << 20)
+#endif
 
 namespace qg {
 namespace host {

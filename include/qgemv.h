@@ -156,12 +156,14 @@ const char *qg_last_kernel(void);
  * codes); rows of 256..2048 columns (any multiple of 256) or of 512..4096
  * (any multiple of 512) form those int32 products on the matrix cores
  * (v_mfma_i32_16x16x64_i8, 16 weight rows per instruction), the same sums
- * bit for bit in int32.  At batch >= 2 (and for batch-1 rows wider than 512 lane tiles)
+ * bit for bit in int32.  Q6_K matrices of 128 MiB or more (the lm_head's
+ * class) run that batch-1 kernel once per row at batch 2 as well.  At
+ * batch >= 2 (and for batch-1 rows wider than 512 lane tiles)
  * the block formats run on the matrix cores with the codes as exact
  * integers (codes at a format's zero point are exact zeros) and f32 sums:
- * at batch 2..4 when the activations fit in LDS (and the matrix is not
- * tall enough for the shared-activation kernel below), and for the
- * over-wide batch-1 rows, as f16 codes with each 256-column chunk of X
+ * at batch 2..4 on rows of at most 1024 columns when the activations fit
+ * in LDS (and the matrix is not tall enough for the shared-activation
+ * kernel below), and for the over-wide batch-1 rows, as f16 codes with each 256-column chunk of X
  * split into f16 hi + lo parts after a power-of-two scaling (relative
  * error < 2^-21 per element); otherwise as bf16 codes with X split into
  * bf16 hi + lo parts (relative error <= 2^-16 per element).  At batch 2..8

@@ -105,11 +105,28 @@ def test_batch_32_full_size_headline_shape():
     (Q4_K, 8448, 3, 2),
 ])
 def test_wide_rows_on_the_matrix_cores(fmt, cols, batch, offset):
-    # rows whose activations do not fit the whole-row LDS image of the
-    # batch-2..4 kernel run on the batched kernel; 8200 rows give a partial
+    # rows wider than 1024 columns run on the batched kernels at every
+    # batch (at batch 2..4 the f16 kernel takes only narrower rows); 8200
+    # rows give a partial
     # last tile, the column ranges of the waves of a tile start at any
     # weight alignment
     _check(fmt, 8200, cols, batch, 3400 + fmt + batch, offset=offset)
+
+
+@pytest.mark.parametrize("fmt,rows,cols,batch", [
+    (Q4_K, 10000, 1024, 3), (Q8_0, 9000, 992, 2), (Q6_K, 300, 768, 4), (Q4_0, 37, 96, 2),
+])
+def test_narrow_rows_at_batch_2_to_4_run_the_f16_kernel(fmt, rows, cols, batch):
+    # rows of at most 1024 columns at batch 2..4: the f16 matrix-core kernel
+    # with the whole row's activations in LDS; 10000 and 9000 rows are more
+    # tiles than two per CU, so the workgroups stream phases of chunks
+    # through two buffers
+    W = _matrix(fmt, rows, cols, 3600 + fmt + batch)
+    X = synth.activations(synth.rng(3601 + fmt + batch), batch, cols)
+    Y = run_gemv(fmt, W, rows, cols, X)
+    assert q.qg_last_kernel() == "mx_f16"
+    Yr, A = oracle.gemv(fmt, W, rows, cols, X)
+    assert_agree(Y, Yr, A, f"f16 kernel fmt {fmt} {rows}x{cols} b{batch}")
 
 
 @pytest.mark.parametrize("fmt,cols,batch", [(Q4_0, 14368, 4), (Q8_0, 12320, 3), (Q4_K, 32768, 1)])

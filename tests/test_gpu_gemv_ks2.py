@@ -8,7 +8,9 @@ format at batch 2, 3, 5 and 8; row counts with a partial last group and a
 partial last tile; an odd chunk count (the two ranges of unequal length)
 with a partial last chunk; weights 2 bytes past 4-byte alignment; the full
 Q5_K 14336 x 4096 workload on sampled rows; zero weights; determinism.
-Tolerance as for every GEMV: |y - y_ref| <= 1e-4 * sum|w x| + 1e-6 per
+Q6_K at batch 2 runs the batch-1 matrix-core kernel once per row where
+that kernel takes the width, so its batch-2 case here has 2304 columns,
+a width that kernel refuses.  Tolerance as for every GEMV: |y - y_ref| <= 1e-4 * sum|w x| + 1e-6 per
 output.
 """
 from __future__ import annotations
@@ -52,7 +54,8 @@ def _check(fmt, rows, cols, batch, seed, offset=0, sample=True):
 @pytest.mark.parametrize("fmt", BLOCK)
 @pytest.mark.parametrize("batch", [2, 3, 5, 8])
 def test_every_format_and_batch(fmt, batch):
-    _check(fmt, ROWS, 1024, batch, 9000 + 10 * fmt + batch)
+    cols = 2304 if fmt == Q6_K and batch <= 2 else 1024
+    _check(fmt, ROWS, cols, batch, 9000 + 10 * fmt + batch)
 
 
 @pytest.mark.parametrize("fmt", BLOCK)
