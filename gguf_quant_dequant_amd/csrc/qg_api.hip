@@ -402,6 +402,7 @@ size_t qgemv_ws_bytes(int fmt, int64_t rows, int64_t cols, int batch) {
     if (g.elems == 0 || fmt == QG_F32 || rows <= 0 || cols <= 0 || cols % g.elems != 0 ||
         batch < 2 || batch > kMaxBatch || rows >= ((int64_t)1 << 31) || cols > 65536)
         return 0;
+    if (ws_uses_qgemv(rows, cols, batch)) return 0;
     // the largest [kg][batch rows][rows] partial-sum block of the call's
     // launches (up to 32 batch rows each; 0 when no launch splits columns
     // across workgroups)
@@ -418,8 +419,10 @@ size_t qgemv_ws_bytes(int fmt, int64_t rows, int64_t cols, int batch) {
 int qgemv_ws(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,
              int batch, void *workspace, size_t workspace_bytes, void *stream) {
     if (const int rcv = check_gemv("qgemv_ws", fmt, W, rows, cols, X, Y, batch)) return rcv;
-    // no batched matrix-core work: qgemv's kernels, no workspace
-    if (fmt == QG_F32 || batch == 1) return qgemv(fmt, W, rows, cols, X, Y, batch, stream);
+    // no batched matrix-core work, or a shape where qgemv's kernels are
+    // faster: qgemv, no workspace
+    if (fmt == QG_F32 || batch == 1 || ws_uses_qgemv(rows, cols, batch))
+        return qgemv(fmt, W, rows, cols, X, Y, batch, stream);
     const size_t need = qgemv_ws_bytes(fmt, rows, cols, batch);
     if (need > 0 && (!workspace || workspace_bytes < need))
         return fail(QG_EINVAL, "qgemv_ws: the workspace holds %zu bytes; this call needs %zu "

@@ -133,6 +133,20 @@ int launch_ws(const void *W, int64_t rows, int64_t cols, const float *X, float *
 
 // qgemv takes the two-range kernel where qgemv_ws would (no workspace is
 // needed there); shorter matrices keep qgemm8_kernel.
+// qgemv_ws at batch 2..8 runs qgemv's kernels instead when its own kernel
+// would split rows of at most 16 chunks across workgroups: there the
+// second kernel that adds the column ranges costs more than qgemm8_kernel
+// loses by sharing no activations (A/B on one box, batch 2 / 8: Q4_K 4096 x
+// 4096 10.1 / 10.6 us against 7.9 / 8.8, Q6_K 9.9 / 12.5 against 9.4 /
+// 10.1, Q8_0 11.2 / 11.8 against 8.5 / 9.4); with more chunks the shared
+// activations win (Q4_0 4096 x 14336, 56 chunks: 17.0 / 17.7 against 18.3
+// / 22.8 us).
+bool ws_uses_qgemv(int64_t rows, int64_t cols, int batch) {
+    const int64_t nchunks = (cols + gm::kChunk - 1) / gm::kChunk;
+    return batch <= 8 && nchunks <= 16 && ws_ks(rows, cols, batch) == 1 &&
+           ws_kg(rows, cols, batch) > 1;
+}
+
 bool gemm_ks2_fits(int fmt, int64_t rows, int64_t cols, int batch) {
     return fmt != QG_F32 && batch >= 2 && ws_ks(rows, cols, batch) == 2;
 }

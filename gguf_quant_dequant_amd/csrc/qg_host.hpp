@@ -296,6 +296,7 @@ int dispatch_down_q8(int fmt, const MoeParams &p, hipStream_t st);
 int try_q6mx(const GemvParams &p, hipStream_t st, bool *done);
 int ws_kg(int64_t rows, int64_t cols, int batch);
 bool gemm_ks2_fits(int fmt, int64_t rows, int64_t cols, int batch);
+bool ws_uses_qgemv(int64_t rows, int64_t cols, int batch);
 int moe_gateup_ws(int fmt, const uint8_t *gate, const uint8_t *up, uint64_t stack_bytes,
                   int64_t rb, int H, int F, int K, int T, int E, const float *x,
                   const double *logits, bool routed, int32_t *sel, float *rw,

@@ -193,7 +193,9 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
  * qgemv's in rounding only).  At batch 2..8 the matrices on which qgemv
  * runs "gemm_ks2_bf16" (4 row tiles per workgroup, two column ranges added
  * in LDS) take that kernel here too, with no workspace (qgemv_ws_bytes 0).
- * F32 and batch 1 run qgemv itself.
+ * F32, batch 1, and batch 2..8 on rows of at most 16 chunks of 256 columns
+ * that this kernel would split over several workgroups (there qgemv's
+ * kernels are faster) run qgemv itself, with no workspace.
  *
  *   workspace        device memory of at least qgemv_ws_bytes(fmt, rows,
  *                    cols, batch) bytes, 16-byte aligned, owned by the
@@ -211,7 +213,8 @@ int qgemv_ws(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
              void *stream);
 
 /* Workspace bytes qgemv_ws needs for these arguments: 0 when none is needed
- * (F32, batch 1, no row split over several workgroups) and for arguments
+ * (F32, batch 1, no row split over several workgroups, the calls that run
+ * qgemv itself) and for arguments
  * qgemv_ws refuses.  Depends only on the arguments, not on the device. */
 size_t qgemv_ws_bytes(int fmt, int64_t rows, int64_t cols, int batch);
 

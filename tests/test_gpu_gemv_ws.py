@@ -7,8 +7,10 @@ rows above), row counts with a partial last group of 8 tiles and a partial
 last tile, rows split over several workgroups (the workspace path) and over
 one (no workspace), a partial last chunk of 256 columns, weights 2 bytes
 past 4-byte alignment, the workload shapes at full size on sampled rows,
-the workspace checks, one workspace reused by calls of other shapes, and
-run-to-run determinism.  Tolerance as for every
+the workspace checks, one workspace reused by calls of other shapes,
+run-to-run determinism, and the batch 2..8 calls on rows of 16 or fewer
+chunks that would be split over workgroups, which run qgemv (no
+workspace, qgemv's bits).  Tolerance as for every
 GEMV: |y - y_ref| <= 1e-4 * sum|w x| + 1e-6 per output.
 """
 from __future__ import annotations
@@ -58,8 +60,9 @@ def _check(fmt, rows, cols, batch, seed, offset=0, want_ws=None):
 @pytest.mark.parametrize("batch", [2, 3, 5, 8, 9, 16, 17, 32, 33, 64])
 def test_every_format_and_batch_with_split_rows(fmt, batch):
     # 300 rows: 19 tiles in 3 groups of 8 (the last partial, its last tile
-    # partial); 4096 columns: 16 chunks over several workgroups
-    cols = 4096
+    # partial); 4352 columns: 17 chunks over several workgroups (at 16 or
+    # fewer, batch 2..8 runs qgemv)
+    cols = 4352
     _check(fmt, 300, cols, batch, 8000 + 100 * fmt + batch, want_ws=True)
 
 
@@ -75,7 +78,7 @@ def test_rows_on_one_workgroup_and_a_partial_chunk(fmt, batch):
 @pytest.mark.parametrize("fmt", BLOCK)
 @pytest.mark.parametrize("batch", [3, 8, 20])
 def test_weights_two_bytes_past_alignment(fmt, batch):
-    cols = 2080 if fmt in (Q8_0, Q4_0) else 2304
+    cols = 4384 if fmt in (Q8_0, Q4_0) else 4608
     _check(fmt, 130, cols, batch, 8200 + 10 * fmt + batch, offset=2)
 
 
@@ -103,7 +106,7 @@ def test_workload_shapes_full_size(name, batch):
 
 
 def test_workspace_checks():
-    rows, cols, batch = 300, 4096, 8
+    rows, cols, batch = 300, 4352, 8
     W = synth.matrix(synth.rng(8400), Q4_K, rows, cols)
     Wd = DeviceBytes(W)
     X = torch.zeros((batch, cols), device=dev())
@@ -126,7 +129,7 @@ def test_workspace_checks():
 
 
 def test_run_to_run_bitwise_identical():
-    rows, cols, batch = 1000, 4096, 8
+    rows, cols, batch = 1000, 4352, 8
     W = synth.matrix(synth.rng(8500), Q5_K, rows, cols)
     X = synth.activations(synth.rng(8501), batch, cols)
     a, _ = run_ws(Q5_K, W, rows, cols, X)
@@ -166,8 +169,8 @@ def test_k_quant_rows_of_zero_weights_give_zero(fmt, batch):
 def test_one_workspace_reused_by_calls_of_other_shapes():
     # no initial contents needed: one workspace of garbage bytes serves calls
     # of other shapes and sizes one after another
-    shapes = [(Q4_0, 300, 4096, 8), (Q4_K, 1000, 4096, 4), (Q5_K, 150, 2048, 16),
-              (Q4_0, 300, 4096, 8), (Q6_K, 600, 4096, 40), (Q4_K, 1000, 4096, 4)]
+    shapes = [(Q4_0, 300, 4352, 8), (Q4_K, 1000, 4352, 4), (Q5_K, 150, 2048, 16),
+              (Q4_0, 300, 4352, 8), (Q6_K, 600, 4096, 40), (Q4_K, 1000, 4352, 4)]
     need = max(q.qgemv_ws_bytes(f, r, c, b) for f, r, c, b in shapes)
     ws = torch.full((need,), 255, dtype=torch.uint8, device=dev())
     for i, (fmt, rows, cols, batch) in enumerate(shapes):
@@ -180,3 +183,28 @@ def test_one_workspace_reused_by_calls_of_other_shapes():
         torch.cuda.synchronize()
         Yr, A = oracle.gemv(fmt, W, rows, cols, X)
         assert_agree(Y.cpu().numpy(), Yr, A, f"reused workspace, call {i}")
+
+
+@pytest.mark.parametrize("fmt", BLOCK)
+@pytest.mark.parametrize("batch", [2, 5, 8])
+def test_short_rows_split_across_workgroups_run_qgemv(fmt, batch):
+    # 300 x 4096 at batch 2..8: 16 chunks that the shared-operand kernel
+    # would split over workgroups; qgemv's kernels run instead, with no
+    # workspace, and give qgemv's bits
+    rows, cols = 300, 4096
+    assert q.qgemv_ws_bytes(fmt, rows, cols, batch) == 0
+    g = synth.rng(8950 + fmt + batch)
+    W = synth.matrix(g, fmt, rows, cols)
+    X = synth.activations(synth.rng(8960 + batch), batch, cols)
+    Y, _ = run_ws(fmt, W, rows, cols, X)
+    assert q.qg_last_kernel() != "gemm_ws_bf16"
+    from gpu_util import run_gemv
+    Y2 = run_gemv(fmt, W, rows, cols, X)
+    assert np.array_equal(Y.view(np.uint32), Y2.view(np.uint32))
+    Yr, A = oracle.gemv(fmt, W, rows, cols, X)
+    assert_agree(Y, Yr, A, f"ws via qgemv fmt {fmt} b{batch}")
+    # at batch 9 the shared-operand kernel takes the same shape
+    X9 = synth.activations(synth.rng(8970), 9, cols)
+    assert q.qgemv_ws_bytes(fmt, rows, cols, 9) > 0
+    run_ws(fmt, W, rows, cols, X9)
+    assert q.qg_last_kernel() == "gemm_ws_bf16"

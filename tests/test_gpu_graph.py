@@ -180,7 +180,7 @@ def test_qgemv_ws_graph_replays_match_eager():
     # kernel (workspace written whole on every call), at batch 8 (packed
     # operands), 24 (two blocks of 16 rows) and 40 (two launches)
     g = synth.rng(995)
-    cases = [(q.QG_Q5_K, 1000, 4096, 8), (q.QG_Q4_0, 300, 4096, 24), (q.QG_Q4_K, 200, 4096, 40)]
+    cases = [(q.QG_Q5_K, 1000, 4352, 8), (q.QG_Q4_0, 300, 4096, 24), (q.QG_Q4_K, 200, 4096, 40)]
     bufs = []
     for fmt, rows, cols, b in cases:
         W = torch.from_numpy(synth.matrix(g, fmt, rows, cols).reshape(-1)).cuda()
