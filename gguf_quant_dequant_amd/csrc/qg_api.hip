@@ -331,10 +331,11 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
         }
     }
     if (gemm_ks2_fits(fmt, rows, cols, batch)) {
-        // tall matrices at batch 2-8: activation operands shared through
+        // tall matrices at batch 2-32: activation operands shared through
         // LDS by a workgroup's 4 tiles, two column ranges per workgroup
         // (Q5_K 14336 x 4096: batch 4 19.5 -> 16.7 us against the f16
-        // kernel, batch 8 24.6 -> 18.1 us against qgemm8_kernel)
+        // kernel, batch 8 24.6 -> 18.1 us against qgemm8_kernel, batch 16
+        // 36.9 -> 24.6 us against qgemm_kernel)
         const int rc = gemm_ks2(fmt, W, rows, cols, X, Y, batch, rb, st);
         if (rc != QG_OK) return rc;
         g_kernel = "gemm_ks2_bf16";
@@ -349,15 +350,23 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
     if (fmt != QG_F32 && batch >= 2) {
         // block formats at batch >= 2: the batched matrix-core kernel, up to
         // 32 batch rows per launch (the weights are read once per launch)
+        // (tall matrices: each launch of 2-32 rows on the two-range kernel)
+        bool ks2_all = true;
         for (int b0 = 0; b0 < batch; b0 += 32) {
             const int nb = batch - b0 < 32 ? batch - b0 : 32;
             const float *Xb = X + (int64_t)b0 * cols;
             float *Yb = Y + (int64_t)b0 * rows;
-            const int rc = nb <= 16 ? gemm_b<1>(fmt, W, rows, cols, Xb, Yb, nb, rb, st)
-                                    : gemm_b<2>(fmt, W, rows, cols, Xb, Yb, nb, rb, st);
+            int rc;
+            if (gemm_ks2_fits(fmt, rows, cols, nb)) {
+                rc = gemm_ks2(fmt, W, rows, cols, Xb, Yb, nb, rb, st);
+            } else {
+                ks2_all = false;
+                rc = nb <= 16 ? gemm_b<1>(fmt, W, rows, cols, Xb, Yb, nb, rb, st)
+                              : gemm_b<2>(fmt, W, rows, cols, Xb, Yb, nb, rb, st);
+            }
             if (rc != QG_OK) return rc;
         }
-        g_kernel = "gemm_bf16";
+        g_kernel = ks2_all ? "gemm_ks2_bf16" : "gemm_bf16";
         return ok();
     }
     if (batch > 8) {

@@ -20,7 +20,7 @@ namespace qg {
 namespace host {
 
 // Two column ranges inside each workgroup of 4 tiles (added in LDS) for
-// tall matrices at batch 8 or less: at least QG_KS2_MIN_WGS such
+// tall matrices (qgemv at batch 2..32, qgemv_ws at 2..16): at least QG_KS2_MIN_WGS such
 // workgroups (one per CU of a 256-CU part, and more) and 4 chunks per row,
 // so that no range is split across workgroups.  Measured at batch 4 / 8,
 // cold weights: Q5_K 14336 x 4096 18.4 / 18.9 us with 8 tiles per
@@ -31,11 +31,26 @@ namespace host {
 #ifndef QG_KS2_MIN_WGS
 #define QG_KS2_MIN_WGS 192
 #endif
-static int ws_ks(int64_t rows, int64_t cols, int batch) {
+// The batch rows up to which qgemv_ws takes the two-range kernel on such
+// matrices (qgemv takes it for every launch of up to 32 rows).  Above 8
+// rows the operands need two or four planes per image, which raises the
+// kernel to ~155 (16 rows) and ~235 VGPRs (32 rows); against qgemm_kernel
+// it still wins (Q5_K 14336 x 4096 at batch 12 / 16 / 24 / 32: 32.2 /
+// 36.9 / 53.6 / 63.1 -> 23.3 / 24.6 / 34.0 / 36.8 us; lm_head 151936 x
+// 2048 at batch 16 / 32: 183 / 309 -> 158 / 227 us), and against the split
+// across workgroups up to 16 rows (batch 12 / 16: 23.8 / 25.1 -> 23.1 /
+// 24.6 us; batch 32: 34.8 -> 36.9 us).
+#ifndef QG_KS2_WS_MAXB
+#define QG_KS2_WS_MAXB 16
+#endif
+static bool ks2_shape(int64_t rows, int64_t cols) {
     const int64_t tiles = (rows + gm::kTileRows - 1) / gm::kTileRows;
     const int64_t groups = (tiles + gw::kWaves / 2 - 1) / (gw::kWaves / 2);
     const int64_t nchunks = (cols + gm::kChunk - 1) / gm::kChunk;
-    return batch <= 8 && QG_KS2_MIN_WGS > 0 && groups >= QG_KS2_MIN_WGS && nchunks >= 4 ? 2 : 1;
+    return QG_KS2_MIN_WGS > 0 && groups >= QG_KS2_MIN_WGS && nchunks >= 4;
+}
+static int ws_ks(int64_t rows, int64_t cols, int batch) {
+    return batch <= QG_KS2_WS_MAXB && ks2_shape(rows, cols) ? 2 : 1;
 }
 
 // Column ranges across workgroups per group of tiles: as many as keep the
@@ -89,7 +104,7 @@ int launch_ws_t(const gw::WsParams &p, hipStream_t st) {
 }
 
 // KS = 2: two column ranges inside each workgroup of 4 tiles and no split
-// across workgroups (no workspace; batch <= 8).
+// across workgroups (no workspace; batch <= 32).
 template <class F, int KS = 1>
 int launch_ws(const void *W, int64_t rows, int64_t cols, const float *X, float *Y, int batch,
               int64_t rb, float *part, int kg, hipStream_t st) {
@@ -113,9 +128,16 @@ int launch_ws(const void *W, int64_t rows, int64_t cols, const float *X, float *
     // multiple of 4 bytes
     const bool ra = !(F::CHUNK % 4 == 0 && rb % 4 == 0 && aligned_to(W, 4));
     if constexpr (KS == 2) {
-        if constexpr (F::CHUNK % 4 == 0)
-            if (!ra) return launch_ws_t<F, 0, false, 2>(p, st);
-        return launch_ws_t<F, 0, true, 2>(p, st);
+        if constexpr (F::CHUNK % 4 == 0) {
+            if (!ra) {
+                if (batch <= 8) return launch_ws_t<F, 0, false, 2>(p, st);
+                if (batch <= 16) return launch_ws_t<F, 1, false, 2>(p, st);
+                return launch_ws_t<F, 2, false, 2>(p, st);
+            }
+        }
+        if (batch <= 8) return launch_ws_t<F, 0, true, 2>(p, st);
+        if (batch <= 16) return launch_ws_t<F, 1, true, 2>(p, st);
+        return launch_ws_t<F, 2, true, 2>(p, st);
     }
     if constexpr (F::CHUNK % 4 == 0) {
         if (!ra) {
@@ -147,8 +169,27 @@ bool ws_uses_qgemv(int64_t rows, int64_t cols, int batch) {
            ws_kg(rows, cols, batch) > 1;
 }
 
+// LDS of the two-range kernel for a format and batch: at 17-32 rows four
+// operand planes per image (128 KiB of images) leave too little room for
+// the weight slots of some formats (Q8_0).
+static size_t ks2_lds(int fmt, int batch) {
+    int chunk = 0;
+    switch (fmt) {
+    case QG_Q4_K: chunk = gm::GK45<false>::CHUNK; break;
+    case QG_Q5_K: chunk = gm::GK45<true>::CHUNK; break;
+    case QG_Q6_K: chunk = gm::GQ6K::CHUNK; break;
+    case QG_Q8_0: chunk = gm::GQ80::CHUNK; break;
+    case QG_Q4_0: chunk = gm::GQ40::CHUNK; break;
+    default: return ~(size_t)0;
+    }
+    const uint32_t slot = 16u * (uint32_t)(gemm_nu(chunk) | 1);
+    return batch <= 8 ? gw::ws_lds_bytes<0, 2>(slot)
+                      : batch <= 16 ? gw::ws_lds_bytes<1, 2>(slot) : gw::ws_lds_bytes<2, 2>(slot);
+}
+
 bool gemm_ks2_fits(int fmt, int64_t rows, int64_t cols, int batch) {
-    return fmt != QG_F32 && batch >= 2 && ws_ks(rows, cols, batch) == 2;
+    return fmt != QG_F32 && batch >= 2 && batch <= 32 && ks2_shape(rows, cols) &&
+           ks2_lds(fmt, batch) <= (size_t)device_lds_max();
 }
 
 int gemm_ks2(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, float *Y,

@@ -166,11 +166,12 @@ const char *qg_last_kernel(void);
  * kernel below), and for the over-wide batch-1 rows, as f16 codes with each 256-column chunk of X
  * split into f16 hi + lo parts after a power-of-two scaling (relative
  * error < 2^-21 per element); otherwise as bf16 codes with X split into
- * bf16 hi + lo parts (relative error <= 2^-16 per element).  At batch 2..8
- * matrices of at least 192 groups of 4 row tiles (12,241 rows or more) and
- * 4 or more 256-column chunks run on a kernel whose workgroups share each
- * activation chunk between 4 row tiles through LDS and add two column
- * ranges in LDS ("gemm_ks2_bf16", no workspace).  qg_last_kernel() names the
+ * bf16 hi + lo parts (relative error <= 2^-16 per element).  Matrices of
+ * at least 192 groups of 4 row tiles (12,241 rows or more) and 4 or more
+ * 256-column chunks run each launch of 2..32 batch rows (Q8_0: 2..16) on a
+ * kernel whose workgroups share each activation chunk between 4 row tiles
+ * through LDS and add two column ranges in LDS ("gemm_ks2_bf16", no
+ * workspace).  qg_last_kernel() names the
  * arithmetic a call used.  Results are
  * deterministic run to run.  Limits: rows < 2^31, cols <= 65536; rows that fit neither
  * kernel (e.g. more than ~64 chunks of 256 columns at batch 1 beyond 512
@@ -190,7 +191,7 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X,
  * row's columns are split over several workgroups; their partial sums go
  * to the workspace and a second kernel adds them per output in a fixed
  * order, so results are deterministic run to run (they differ from
- * qgemv's in rounding only).  At batch 2..8 the matrices on which qgemv
+ * qgemv's in rounding only).  At batch 2..16 the matrices on which qgemv
  * runs "gemm_ks2_bf16" (4 row tiles per workgroup, two column ranges added
  * in LDS) take that kernel here too, with no workspace (qgemv_ws_bytes 0).
  * F32, batch 1, and batch 2..8 on rows of at most 16 chunks of 256 columns

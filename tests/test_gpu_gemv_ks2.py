@@ -1,10 +1,14 @@
-"""GPU parity of qgemv's batch 2-8 kernel for tall matrices (activation
+"""GPU parity of qgemv's batch 2-32 kernel for tall matrices (activation
 operands shared through LDS by a workgroup's 4 row tiles, two column ranges
 per workgroup added through LDS, no workspace) against the oracle.
 
 qgemv takes it when the matrix has at least 192 groups of 4 row tiles
-(12,241 rows or more) and 4 or more chunks of 256 columns.  Every block
-format at batch 2, 3, 5 and 8; row counts with a partial last group and a
+(12,241 rows or more) and 4 or more chunks of 256 columns, for every
+launch of 2 to 32 batch rows; qgemv_ws up to 16 rows.  Every block
+format at batch 2, 3, 5 and 8 (one operand plane), 9, 16 (two), 17, 24 and
+32 (four, the second block of 16 rows partial or whole; Q8_0 there on
+the other kernel, its LDS need too large), 40 (two launches)
+and 33 (a last launch of one row on the other kernel); row counts with a partial last group and a
 partial last tile; an odd chunk count (the two ranges of unequal length)
 with a partial last chunk; weights 2 bytes past 4-byte alignment; the full
 Q5_K 14336 x 4096 workload on sampled rows; zero weights; determinism.
@@ -39,11 +43,11 @@ def _sampled(rows, seed):
                                      g.integers(0, rows, 400)]))
 
 
-def _check(fmt, rows, cols, batch, seed, offset=0, sample=True):
+def _check(fmt, rows, cols, batch, seed, offset=0, sample=True, kernel="gemm_ks2_bf16"):
     W = synth.matrix(synth.rng(seed), fmt, rows, cols)
     X = synth.activations(synth.rng(seed + 1), batch, cols)
     Y = run_gemv(fmt, W, rows, cols, X, offset=offset)
-    assert q.qg_last_kernel() == "gemm_ks2_bf16"
+    assert q.qg_last_kernel() == kernel
     idx = _sampled(rows, seed) if sample else None
     Yr, A = oracle.gemv(fmt, W, rows, cols, X, row_idx=idx)
     Yg = Y[:, idx] if sample else Y
@@ -120,3 +124,52 @@ def test_run_to_run_bitwise_identical():
     a = run_gemv(Q5_K, W, ROWS, 1024, X)
     b = run_gemv(Q5_K, W, ROWS, 1024, X, offset=0)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+@pytest.mark.parametrize("fmt", BLOCK)
+@pytest.mark.parametrize("batch", [9, 16, 17, 24, 32])
+def test_every_format_above_eight_rows(fmt, batch):
+    # Q8_0's weight slots leave no room for the four-plane images of 17-32
+    # rows in LDS: there it runs the other batched kernel
+    kernel = "gemm_bf16" if fmt == Q8_0 and batch > 16 else "gemm_ks2_bf16"
+    _check(fmt, ROWS, 1024, batch, 9500 + 10 * fmt + batch, kernel=kernel)
+
+
+@pytest.mark.parametrize("fmt", [Q4_K, Q4_0])
+def test_two_launches(fmt):
+    # 40 rows: launches of 32 and 8 rows, both on the two-range kernel
+    _check(fmt, ROWS, 1280, 40, 9600 + fmt)
+
+
+def test_a_last_launch_of_one_row_runs_the_other_kernel():
+    W = synth.matrix(synth.rng(9700), Q4_K, ROWS, 1024)
+    X = synth.activations(synth.rng(9701), 33, 1024)
+    Y = run_gemv(Q4_K, W, ROWS, 1024, X)
+    assert q.qg_last_kernel() == "gemm_bf16"
+    idx = _sampled(ROWS, 9700)
+    Yr, A = oracle.gemv(Q4_K, W, ROWS, 1024, X, row_idx=idx)
+    assert_agree(Y[:, idx], Yr, A, "ks2 b33 (32 + 1)")
+
+
+@pytest.mark.parametrize("batch,two_range", [(12, True), (16, True), (17, False), (32, False)])
+def test_qgemv_ws_takes_it_up_to_sixteen_rows(batch, two_range):
+    from gpu_util import DeviceBytes, dev
+    W = synth.matrix(synth.rng(9800 + batch), Q5_K, ROWS, 1024)
+    X = synth.activations(synth.rng(9801 + batch), batch, 1024)
+    need = q.qgemv_ws_bytes(Q5_K, ROWS, 1024, batch)
+    assert (need == 0) == two_range
+    Wd = DeviceBytes(W)
+    Xd = torch.from_numpy(X).to(dev())
+    Yd = torch.full((batch, ROWS), float("nan"), device=dev())
+    ws = torch.full((need,), 255, dtype=torch.uint8, device=dev()) if need else None
+    q.qgemv_ws(Q5_K, Wd.ptr, ROWS, 1024, Xd, Yd, batch, ws)
+    torch.cuda.synchronize()
+    Y = Yd.cpu().numpy()
+    assert q.qg_last_kernel() == "gemm_ws_bf16"
+    idx = _sampled(ROWS, 9800 + batch)
+    Yr, A = oracle.gemv(Q5_K, W, ROWS, 1024, X, row_idx=idx)
+    assert_agree(Y[:, idx], Yr, A, f"qgemv_ws b{batch}")
+    if two_range:
+        # the same kernel as qgemv: the same bits
+        Y2 = run_gemv(Q5_K, W, ROWS, 1024, X)
+        assert np.array_equal(Y.view(np.uint32), Y2.view(np.uint32))
