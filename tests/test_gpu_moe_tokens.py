@@ -2,7 +2,10 @@
 own, expert GEMVs grouped by expert) against the oracle, which runs the
 MoE FFN token by token.
 
-Per token: the selection bit for bit, route weights to 1e-6 relative, the
+Formats, T = 2..8, 64 routes over up to 1024 experts (routed in the
+gate/up workgroups and routed ahead), shared and identical tokens, one
+token, the Qwen3 shape on all 64 bench tokens, a non-finite token, wide
+hidden rows.  Per token: the selection bit for bit, route weights to 1e-6 relative, the
 router logits to 1e-12 of sum |R x|, and every output row to
 1e-4 * (|residual| + sum_s sum_j |D a|) + 1e-6.
 """
@@ -84,6 +87,17 @@ def test_small_tokens_every_format(gate_fmt, down_fmt, T):
     x = synth.activations(g, T, m.H)
     res = synth.activations(g, T, m.H)
     _compare(m, x, res, f"tokens {T} {gate_fmt}/{down_fmt}")
+
+
+@pytest.mark.parametrize("E,k,T", [(1024, 8, 8), (1000, 32, 2), (130, 16, 4)])
+def test_sixty_four_routes_over_many_experts(E, k, T):
+    # the most routes a call takes (T * k = 64): 1024 experts routed ahead
+    # (the distinct-expert search over 1024 words of LDS), 1000 experts (not
+    # a multiple of 64) and 130 routed in the gate/up workgroups
+    m, g = _small(q.QG_Q4_K, q.QG_Q8_0, E=E, k=k, H=256, F=64, seed=71 + E + k)
+    x = synth.activations(g, T, m.H)
+    res = synth.activations(g, T, m.H)
+    _compare(m, x, res, f"E {E} k {k} T {T}")
 
 
 def test_tokens_sharing_every_expert_and_alias():
