@@ -305,27 +305,24 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
     if (QG_Q6_MX && fmt == QG_Q6_K &&
         (batch == 1 ||
          (batch <= QG_Q6_MX_ROWS && (uint64_t)rows * (uint64_t)rb >= QG_Q6_MX_ROWS_BYTES))) {
-        // batch 1, and on matrices of the lm_head's class batch 2 as two
-        // batch-1 launches: the bf16 kernels run Q6_K rows at ~2.2 TB/s
-        // (lm_head 151936 x 2048 at batch 2: 117 us against 2 x 43.5),
-        // the batch-1 kernel reaches its rate only on such sizes (14336 x
-        // 4096 at batch 2: 21.4 us on the bf16 kernel, 34.1 as two launches)
-        for (int b = 0; b < batch; b++) {
-            GemvParams p{};
-            p.W = (const uint8_t *)W;
-            p.X = X + (int64_t)b * cols;
-            p.Y = Y + (int64_t)b * rows;
-            p.rows = rows;
-            p.w_bytes = (uint64_t)rows * (uint64_t)rb;
-            p.row_bytes = (uint32_t)rb;
-            p.cols = (uint32_t)cols;
-            p.batch_x = 1;
-            // the shape decides whether it fits, the same for every row
-            const int qrc = try_q6mx(p, st, &done);
-            if (!done) break;
-            if (qrc != QG_OK) return qrc;
-        }
+        // batch 1, and batch 2 on matrices of 16 MiB or more: the int8
+        // digit-plane kernel, at batch 2 with both rows' planes against each
+        // tile's codes (A/B on one box, batch 2: lm_head 151936 x 2048 117
+        // us on the bf16 kernel, 86.5 as two batch-1 launches, 48.5; 32768
+        // x 2048 26.1 -> 16.8; 14336 x 4096 21.5 -> 20.2; smaller matrices
+        // keep the other kernels: 4096 x 4096 9.4 against 11.2)
+        GemvParams p{};
+        p.W = (const uint8_t *)W;
+        p.X = X;
+        p.Y = Y;
+        p.rows = rows;
+        p.w_bytes = (uint64_t)rows * (uint64_t)rb;
+        p.row_bytes = (uint32_t)rb;
+        p.cols = (uint32_t)cols;
+        p.batch_x = 1;
+        const int qrc = try_q6mx(p, batch, st, &done);
         if (done) {
+            if (qrc != QG_OK) return qrc;
             g_kernel = "mfma_i8_q6k";
             return ok();
         }

@@ -63,13 +63,13 @@
 #ifndef QG_Q6_MX
 #define QG_Q6_MX 1
 #endif
-// Batch rows up to which Q6_K runs the batch-1 kernel once per row, on
-// matrices of at least QG_Q6_MX_ROWS_BYTES.
+// Batch rows up to which Q6_K runs that kernel (two rows: the weights read
+// once for both), on matrices of at least QG_Q6_MX_ROWS_BYTES.
 #ifndef QG_Q6_MX_ROWS
 #define QG_Q6_MX_ROWS 2
 #endif
 #ifndef QG_Q6_MX_ROWS_BYTES
-#define QG_Q6_MX_ROWS_BYTES (128ull << 20)
+#define QG_Q6_MX_ROWS_BYTES (16ull << 20)
 #endif
 
 namespace qg {
@@ -293,7 +293,7 @@ int dispatch_gateup(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_down(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_gateup_q8(int fmt, const MoeParams &p, hipStream_t st);
 int dispatch_down_q8(int fmt, const MoeParams &p, hipStream_t st);
-int try_q6mx(const GemvParams &p, hipStream_t st, bool *done);
+int try_q6mx(const GemvParams &p, int nb, hipStream_t st, bool *done);
 int ws_kg(int64_t rows, int64_t cols, int batch);
 bool gemm_ks2_fits(int fmt, int64_t rows, int64_t cols, int batch);
 bool ws_uses_qgemv(int64_t rows, int64_t cols, int batch);

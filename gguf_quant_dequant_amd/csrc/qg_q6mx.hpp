@@ -124,10 +124,13 @@ __device__ __forceinline__ v4i codes(const Fields &f) {
     return B;
 }
 
-template <int TPW>
-__global__ void __launch_bounds__(512) q6k_mx1_kernel(GemvParams p) {
+// NB batch rows (1 or 2): the rows of X lie one after another (cols floats
+// each) and are staged together; every tile's codes are assembled once and
+// meet each row's digit planes in an instruction of its own.
+template <int TPW, int NB>
+__device__ __forceinline__ void q6k_mx_body(const GemvParams &p) {
     extern __shared__ __attribute__((aligned(16))) uint32_t stage[];
-    __shared__ float red[8][kRows];
+    __shared__ float red[NB][8][kRows];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int nw = (int)(blockDim.x >> 6);
     const int n = lane & 15, kg = lane >> 4;  // B and D roles: row n, l quad / group kg
@@ -135,7 +138,7 @@ __global__ void __launch_bounds__(512) q6k_mx1_kernel(GemvParams p) {
     const uint32_t nthr = blockDim.x;
 
     // the activations' loads, then the first block's weight loads
-    const uint32_t xtot = p.cols;
+    const uint32_t xtot = p.cols * (uint32_t)NB;
     const rsrc_t rx = make_rsrc(p.X, 4u * xtot);
     uint32_t xr[kStageChunks][4];
     xs_fetch(rx, 0u, xtot / 4u, tid, nthr, xr);
@@ -147,13 +150,16 @@ __global__ void __launch_bounds__(512) q6k_mx1_kernel(GemvParams p) {
     // A operands and run scales of this wave's tiles
     xs_commit(stage, tid, nthr, xr);
     __syncthreads();
-    v4i A[TPW];
-    float fr[TPW];  // 2^-s of run (tile, group kg)
+    v4i A[NB][TPW];
+    float fr[NB][TPW];  // 2^-s of run (tile, group kg) of batch row b
+#pragma unroll
+    for (int b = 0; b < NB; b++)
 #pragma unroll
     for (int i = 0; i < TPW; i++) {
         const int t = wave * TPW + i;
         const int sb = t >> 2, h = (t >> 1) & 1, l0 = (t & 1) * 16;
-        const uint32_t c = (uint32_t)(256 * sb + 128 * h + 32 * ar + l0 + 4 * kg);
+        const uint32_t c = (uint32_t)b * p.cols +
+                           (uint32_t)(256 * sb + 128 * h + 32 * ar + l0 + 4 * kg);
         const uint32_t *q4 = stage + 4 * xs_pos(c / 4u);
         float x[4];
         uint32_t mb = 0;
@@ -172,12 +178,12 @@ __global__ void __launch_bounds__(512) q6k_mx1_kernel(GemvParams p) {
         float f;
         digits4(x, mb, pl, &f);
         const uint32_t mine = ap == 0 ? pl[0] : ap == 1 ? pl[1] : ap == 2 ? pl[2] : 0u;
-        A[i][0] = (int)(ar == 0 ? mine : 0u);
-        A[i][1] = (int)(ar == 1 ? mine : 0u);
-        A[i][2] = (int)(ar == 2 ? mine : 0u);
-        A[i][3] = (int)(ar == 3 ? mine : 0u);
+        A[b][i][0] = (int)(ar == 0 ? mine : 0u);
+        A[b][i][1] = (int)(ar == 1 ? mine : 0u);
+        A[b][i][2] = (int)(ar == 2 ? mine : 0u);
+        A[b][i][3] = (int)(ar == 3 ? mine : 0u);
         // the scale of run (t, kg) is held by lane 4 kg (group kg, plane 0)
-        fr[i] = __shfl(f, 4 * kg);
+        fr[b][i] = __shfl(f, 4 * kg);
     }
     __syncthreads();
 
@@ -193,35 +199,63 @@ __global__ void __launch_bounds__(512) q6k_mx1_kernel(GemvParams p) {
             stage_fetch(cur, tid, nthr, reg);
         }
         const uint32_t rowoff = d16 + (uint32_t)n * p.row_bytes;
-        float acc = 0.f;
+        float acc[NB];
+#pragma unroll
+        for (int b = 0; b < NB; b++) acc[b] = 0.f;
         // tile i's fields, read one tile ahead of its instruction; a
         // tile's scaling waits for the next tile's instruction to issue
         Fields fd[TPW];
         fetch<TPW>(stage, rowoff, wave, kg, 0, fd[0]);
-        v4i Dp = zero;
+        v4i Dp[NB];
+#pragma unroll
+        for (int b = 0; b < NB; b++) Dp[b] = zero;
 #pragma unroll
         for (int i = 0; i < TPW; i++) {
             if (i + 1 < TPW) fetch<TPW>(stage, rowoff, wave, kg, i + 1, fd[i + 1]);
-            const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[i], codes(fd[i]), zero, 0, 0, 0);
-            if (i > 0) acc = fmaf(fd[i - 1].ds * fr[i - 1], digits_sum(Dp[0], Dp[1], Dp[2]), acc);
-            Dp = D;
+            const v4i Bc = codes(fd[i]);
+#pragma unroll
+            for (int b = 0; b < NB; b++) {
+                const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[b][i], Bc, zero, 0, 0, 0);
+                if (i > 0)
+                    acc[b] = fmaf(fd[i - 1].ds * fr[b][i - 1],
+                                  digits_sum(Dp[b][0], Dp[b][1], Dp[b][2]), acc[b]);
+                Dp[b] = D;
+            }
         }
-        acc = fmaf(fd[TPW - 1].ds * fr[TPW - 1], digits_sum(Dp[0], Dp[1], Dp[2]), acc);
         // the four groups of row n (lanes n, n + 16, n + 32, n + 48), then
         // the waves in order
-        acc += __shfl_xor(acc, 16);
-        acc += __shfl_xor(acc, 32);
-        if (lane < kRows) red[wave][lane] = acc;
+#pragma unroll
+        for (int b = 0; b < NB; b++) {
+            acc[b] = fmaf(fd[TPW - 1].ds * fr[b][TPW - 1],
+                          digits_sum(Dp[b][0], Dp[b][1], Dp[b][2]), acc[b]);
+            acc[b] += __shfl_xor(acc[b], 16);
+            acc[b] += __shfl_xor(acc[b], 32);
+            if (lane < kRows) red[b][wave][lane] = acc[b];
+        }
         __syncthreads();
         // red is rewritten only after the next block's first barrier, which
         // these threads reach after reading it
         const int64_t r0 = it * kRows;
-        if (tid < kRows && r0 + tid < p.rows) {
-            float s = red[0][tid];
-            for (int w = 1; w < nw; w++) s += red[w][tid];
-            p.Y[r0 + tid] = s;
+        if (tid < NB * kRows) {
+            const int b = tid / kRows, rr = tid % kRows;
+            if (r0 + rr < p.rows) {
+                float s = red[b][0][rr];
+                for (int w = 1; w < nw; w++) s += red[b][w][rr];
+                p.Y[(int64_t)b * p.rows + r0 + rr] = s;
+            }
         }
     }
+}
+
+template <int TPW>
+__global__ void __launch_bounds__(512) q6k_mx1_kernel(GemvParams p) {
+    q6k_mx_body<TPW, 1>(p);
+}
+
+// Two batch rows: the weights are read once for both.
+template <int TPW>
+__global__ void __launch_bounds__(512) q6k_mx2_kernel(GemvParams p) {
+    q6k_mx_body<TPW, 2>(p);
 }
 
 }  // namespace q6mx

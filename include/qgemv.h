@@ -156,8 +156,9 @@ const char *qg_last_kernel(void);
  * codes); rows of 256..2048 columns (any multiple of 256) or of 512..4096
  * (any multiple of 512) form those int32 products on the matrix cores
  * (v_mfma_i32_16x16x64_i8, 16 weight rows per instruction), the same sums
- * bit for bit in int32.  Q6_K matrices of 128 MiB or more (the lm_head's
- * class) run that batch-1 kernel once per row at batch 2 as well.  At
+ * bit for bit in int32.  Q6_K matrices of 16 MiB or more run the same
+ * kernel at batch 2, both rows against each tile's codes (the weights read
+ * once; each row's result bit-identical to its batch-1 result).  At
  * batch >= 2 (and for batch-1 rows wider than 512 lane tiles)
  * the block formats run on the matrix cores with the codes as exact
  * integers (codes at a format's zero point are exact zeros) and f32 sums:

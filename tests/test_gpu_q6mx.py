@@ -5,10 +5,10 @@ Every row width the kernel takes (multiples of 256 columns up to 2048, of
 512 up to 4096: one to eight waves per workgroup, four or eight 64-column
 tiles per wave), row counts with a partial last block of 16 rows, weights
 at 0 and 2 bytes past 4-byte alignment (rows of 210 bytes put odd rows at
-2 mod 4), and the width the kernel does not take.  At batch 2 the
-lm_head (255 MB) runs the kernel once per row (a row bit-identical to its
-batch-1 result; sampled rows against the oracle), smaller matrices and
-batch 3 the batched kernels.  Tolerance as for every
+2 mod 4), and the width the kernel does not take.  At batch 2 matrices of
+16 MiB or more (the lm_head on sampled rows, three widths on every row)
+run the two-row kernel, each row bit-identical to its batch-1 result;
+smaller matrices the batched kernels.  Tolerance as for every
 GEMV: |y - y_ref| <= 1e-4 * sum|w x| + 1e-6 per output.
 """
 from __future__ import annotations
@@ -108,8 +108,8 @@ def test_batch_two_on_smaller_matrices_runs_the_batched_kernels(rows, cols):
 
 
 def test_lm_head_batch_two_sampled_rows():
-    # 255 MB of weights: batch 2 runs the batch-1 kernel once per row, so
-    # each row of the result is its batch-1 result bit for bit
+    # 255 MB of weights: batch 2 runs the two-row kernel, whose every row is
+    # its batch-1 result bit for bit (the same sums in the same order)
     case = synth.GEMV_CASES["q6_k_151936x2048"]
     W, X = synth.gemv_inputs(case, 2)
     Y = run_gemv(case.fmt, W, case.rows, case.cols, X)
@@ -120,4 +120,20 @@ def test_lm_head_batch_two_sampled_rows():
     Yr, A = oracle.gemv(case.fmt, W, case.rows, case.cols, X, row_idx=idx)
     assert_agree(Y[:, idx], Yr, A, "lm_head batch 2 sampled rows")
     Y1 = run_gemv(case.fmt, W, case.rows, case.cols, X[1:2])
+    assert np.array_equal(Y[1:2].view(np.uint32), Y1.view(np.uint32))
+
+
+@pytest.mark.parametrize("rows,cols,offset", [(10240, 2048, 0), (14000, 1536, 2), (5200, 4096, 0)])
+def test_two_row_kernel(rows, cols, offset):
+    # matrices of 16 MiB or more at batch 2: both rows against each tile's
+    # codes (eight, three and eight waves per workgroup), every output row
+    seed = 7600 + cols // 256
+    W = synth.matrix(synth.rng(seed), Q6_K, rows, cols)
+    assert W.nbytes >= 16 << 20
+    X = synth.activations(synth.rng(seed + 1), 2, cols)
+    Y = run_gemv(Q6_K, W, rows, cols, X, offset=offset)
+    assert q.qg_last_kernel() == "mfma_i8_q6k"
+    Yr, A = oracle.gemv(Q6_K, W, rows, cols, X)
+    assert_agree(Y, Yr, A, f"q6_k two rows {rows}x{cols} off{offset}")
+    Y1 = run_gemv(Q6_K, W, rows, cols, X[1:2], offset=offset)
     assert np.array_equal(Y[1:2].view(np.uint32), Y1.view(np.uint32))
