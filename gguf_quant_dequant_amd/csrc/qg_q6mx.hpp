@@ -124,8 +124,8 @@ __device__ __forceinline__ v4i codes(const Fields &f) {
     return B;
 }
 
-// NB batch rows (1 or 2): the rows of X lie one after another (cols floats
-// each) and are staged together; every tile's codes are assembled once and
+// NB batch rows (2): the rows of X lie one after another (cols floats each)
+// and are staged together; every tile's codes are assembled once and
 // meet each row's digit planes in an instruction of its own.
 template <int TPW, int NB>
 __device__ __forceinline__ void q6k_mx_body(const GemvParams &p) {
@@ -247,9 +247,106 @@ __device__ __forceinline__ void q6k_mx_body(const GemvParams &p) {
     }
 }
 
+// One batch row: the same steps written out for a single row (compiled
+// through the two-row body it took 0.5 us longer on the lm_head).
 template <int TPW>
 __global__ void __launch_bounds__(512) q6k_mx1_kernel(GemvParams p) {
-    q6k_mx_body<TPW, 1>(p);
+    extern __shared__ __attribute__((aligned(16))) uint32_t stage[];
+    __shared__ float red[8][kRows];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int nw = (int)(blockDim.x >> 6);
+    const int n = lane & 15, kg = lane >> 4;  // B and D roles: row n, l quad / group kg
+    const int ar = n >> 2, ap = n & 3;        // A role: group ar, plane ap (3: none)
+    const uint32_t nthr = blockDim.x;
+
+    // the activations' loads, then the first block's weight loads
+    const uint32_t xtot = p.cols;
+    const rsrc_t rx = make_rsrc(p.X, 4u * xtot);
+    uint32_t xr[kStageChunks][4];
+    xs_fetch(rx, 0u, xtot / 4u, tid, nthr, xr);
+    int64_t it = blockIdx.x;
+    uint32_t reg[kStageChunks][4];
+    StageBlock cur = stage_block(p, it, kRows);
+    stage_fetch(cur, tid, nthr, reg);
+
+    // A operands and run scales of this wave's tiles
+    xs_commit(stage, tid, nthr, xr);
+    __syncthreads();
+    v4i A[TPW];
+    float fr[TPW];  // 2^-s of run (tile, group kg)
+#pragma unroll
+    for (int i = 0; i < TPW; i++) {
+        const int t = wave * TPW + i;
+        const int sb = t >> 2, h = (t >> 1) & 1, l0 = (t & 1) * 16;
+        const uint32_t c = (uint32_t)(256 * sb + 128 * h + 32 * ar + l0 + 4 * kg);
+        const uint32_t *q4 = stage + 4 * xs_pos(c / 4u);
+        float x[4];
+        uint32_t mb = 0;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            x[j] = __builtin_bit_cast(float, q4[j]);
+            const uint32_t a = q4[j] & 0x7FFFFFFFu;
+            mb = a > mb ? a : mb;
+        }
+        // the run's 16 columns lie in lanes n, n + 16, n + 32, n + 48
+        uint32_t o = (uint32_t)__shfl_xor((int)mb, 16);
+        mb = o > mb ? o : mb;
+        o = (uint32_t)__shfl_xor((int)mb, 32);
+        mb = o > mb ? o : mb;
+        uint32_t pl[3];
+        float f;
+        digits4(x, mb, pl, &f);
+        const uint32_t mine = ap == 0 ? pl[0] : ap == 1 ? pl[1] : ap == 2 ? pl[2] : 0u;
+        A[i][0] = (int)(ar == 0 ? mine : 0u);
+        A[i][1] = (int)(ar == 1 ? mine : 0u);
+        A[i][2] = (int)(ar == 2 ? mine : 0u);
+        A[i][3] = (int)(ar == 3 ? mine : 0u);
+        // the scale of run (t, kg) is held by lane 4 kg (group kg, plane 0)
+        fr[i] = __shfl(f, 4 * kg);
+    }
+    __syncthreads();
+
+    const v4i zero = {0, 0, 0, 0};
+    for (; it * kRows < p.rows; it += gridDim.x) {
+        // every wave has finished reading the previous block (the barrier
+        // after its red writes), so the stage can be overwritten
+        stage_store(stage, tid, nthr, reg);
+        __syncthreads();
+        const uint32_t d16 = cur.d16;
+        if ((it + gridDim.x) * kRows < p.rows) {
+            cur = stage_block(p, it + gridDim.x, kRows);
+            stage_fetch(cur, tid, nthr, reg);
+        }
+        const uint32_t rowoff = d16 + (uint32_t)n * p.row_bytes;
+        float acc = 0.f;
+        // tile i's fields, read one tile ahead of its instruction; a
+        // tile's scaling waits for the next tile's instruction to issue
+        Fields fd[TPW];
+        fetch<TPW>(stage, rowoff, wave, kg, 0, fd[0]);
+        v4i Dp = zero;
+#pragma unroll
+        for (int i = 0; i < TPW; i++) {
+            if (i + 1 < TPW) fetch<TPW>(stage, rowoff, wave, kg, i + 1, fd[i + 1]);
+            const v4i D = __builtin_amdgcn_mfma_i32_16x16x64_i8(A[i], codes(fd[i]), zero, 0, 0, 0);
+            if (i > 0) acc = fmaf(fd[i - 1].ds * fr[i - 1], digits_sum(Dp[0], Dp[1], Dp[2]), acc);
+            Dp = D;
+        }
+        acc = fmaf(fd[TPW - 1].ds * fr[TPW - 1], digits_sum(Dp[0], Dp[1], Dp[2]), acc);
+        // the four groups of row n (lanes n, n + 16, n + 32, n + 48), then
+        // the waves in order
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        if (lane < kRows) red[wave][lane] = acc;
+        __syncthreads();
+        // red is rewritten only after the next block's first barrier, which
+        // these threads reach after reading it
+        const int64_t r0 = it * kRows;
+        if (tid < kRows && r0 + tid < p.rows) {
+            float s = red[0][tid];
+            for (int w = 1; w < nw; w++) s += red[w][tid];
+            p.Y[r0 + tid] = s;
+        }
+    }
 }
 
 // Two batch rows: the weights are read once for both.
