@@ -302,27 +302,35 @@ int qgemv(int fmt, const void *W, int64_t rows, int64_t cols, const float *X, fl
     hipStream_t st = (hipStream_t)stream;
     if (const int rc0 = no_pending_error("qgemv")) return rc0;
     bool done = false;
+    const uint64_t wbytes = (uint64_t)rows * (uint64_t)rb;
     if (QG_Q6_MX && fmt == QG_Q6_K &&
-        (batch == 1 ||
-         (batch <= QG_Q6_MX_ROWS && (uint64_t)rows * (uint64_t)rb >= QG_Q6_MX_ROWS_BYTES))) {
+        (batch == 1 || (batch <= QG_Q6_MX_ROWS && wbytes >= QG_Q6_MX_ROWS_BYTES) ||
+         (batch <= QG_Q6_MX_PAIRS && wbytes >= QG_Q6_MX_PAIRS_BYTES))) {
         // batch 1, and batch 2 on matrices of 16 MiB or more: the int8
         // digit-plane kernel, at batch 2 with both rows' planes against each
         // tile's codes (A/B on one box, batch 2: lm_head 151936 x 2048 117
         // us on the bf16 kernel, 86.5 as two batch-1 launches, 48.5; 32768
         // x 2048 26.1 -> 16.8; 14336 x 4096 21.5 -> 20.2; smaller matrices
-        // keep the other kernels: 4096 x 4096 9.4 against 11.2)
-        GemvParams p{};
-        p.W = (const uint8_t *)W;
-        p.X = X;
-        p.Y = Y;
-        p.rows = rows;
-        p.w_bytes = (uint64_t)rows * (uint64_t)rb;
-        p.row_bytes = (uint32_t)rb;
-        p.cols = (uint32_t)cols;
-        p.batch_x = 1;
-        const int qrc = try_q6mx(p, batch, st, &done);
-        if (done) {
+        // keep the other kernels: 4096 x 4096 9.4 against 11.2); on the
+        // lm_head's class batch 3-4 as launches of two rows and one
+        for (int b0 = 0; b0 < batch; b0 += 2) {
+            const int nb = batch - b0 < 2 ? batch - b0 : 2;
+            GemvParams p{};
+            p.W = (const uint8_t *)W;
+            p.X = X + (int64_t)b0 * cols;
+            p.Y = Y + (int64_t)b0 * rows;
+            p.rows = rows;
+            p.w_bytes = wbytes;
+            p.row_bytes = (uint32_t)rb;
+            p.cols = (uint32_t)cols;
+            p.batch_x = 1;
+            // the shape decides whether the kernel takes it, for one row
+            // and two alike
+            const int qrc = try_q6mx(p, nb, st, &done);
+            if (!done) break;
             if (qrc != QG_OK) return qrc;
+        }
+        if (done) {
             g_kernel = "mfma_i8_q6k";
             return ok();
         }

@@ -71,6 +71,14 @@
 #ifndef QG_Q6_MX_ROWS_BYTES
 #define QG_Q6_MX_ROWS_BYTES (16ull << 20)
 #endif
+// Batch rows up to which Q6_K matrices of at least QG_Q6_MX_PAIRS_BYTES run
+// it as launches of two rows (and one).
+#ifndef QG_Q6_MX_PAIRS
+#define QG_Q6_MX_PAIRS 4
+#endif
+#ifndef QG_Q6_MX_PAIRS_BYTES
+#define QG_Q6_MX_PAIRS_BYTES (128ull << 20)
+#endif
 
 namespace qg {
 namespace host {

@@ -158,7 +158,8 @@ const char *qg_last_kernel(void);
  * (v_mfma_i32_16x16x64_i8, 16 weight rows per instruction), the same sums
  * bit for bit in int32.  Q6_K matrices of 16 MiB or more run the same
  * kernel at batch 2, both rows against each tile's codes (the weights read
- * once; each row's result bit-identical to its batch-1 result).  At
+ * once; each row's result bit-identical to its batch-1 result), and those
+ * of 128 MiB or more at batch 3..4 as launches of two rows and one.  At
  * batch >= 2 (and for batch-1 rows wider than 512 lane tiles)
  * the block formats run on the matrix cores with the codes as exact
  * integers (codes at a format's zero point are exact zeros) and f32 sums:

@@ -8,7 +8,8 @@ at 0 and 2 bytes past 4-byte alignment (rows of 210 bytes put odd rows at
 2 mod 4), and the width the kernel does not take.  At batch 2 matrices of
 16 MiB or more (the lm_head on sampled rows, three widths on every row)
 run the two-row kernel, each row bit-identical to its batch-1 result;
-smaller matrices the batched kernels.  Tolerance as for every
+smaller matrices the batched kernels; the lm_head at batch 3 and 4 runs
+launches of two rows and one.  Tolerance as for every
 GEMV: |y - y_ref| <= 1e-4 * sum|w x| + 1e-6 per output.
 """
 from __future__ import annotations
@@ -137,3 +138,21 @@ def test_two_row_kernel(rows, cols, offset):
     assert_agree(Y, Yr, A, f"q6_k two rows {rows}x{cols} off{offset}")
     Y1 = run_gemv(Q6_K, W, rows, cols, X[1:2], offset=offset)
     assert np.array_equal(Y[1:2].view(np.uint32), Y1.view(np.uint32))
+
+
+@pytest.mark.parametrize("batch", [3, 4])
+def test_lm_head_batch_three_and_four(batch):
+    # 255 MB of weights at batch 3-4: launches of two rows and one, every
+    # row bit-identical to its batch-1 result
+    case = synth.GEMV_CASES["q6_k_151936x2048"]
+    W, X = synth.gemv_inputs(case, batch)
+    Y = run_gemv(case.fmt, W, case.rows, case.cols, X)
+    assert q.qg_last_kernel() == "mfma_i8_q6k"
+    g = np.random.default_rng(93 + batch)
+    idx = np.unique(np.concatenate([g.integers(0, case.rows, 600),
+                                    np.arange(16), np.arange(case.rows - 16, case.rows)]))
+    Yr, A = oracle.gemv(case.fmt, W, case.rows, case.cols, X, row_idx=idx)
+    assert_agree(Y[:, idx], Yr, A, f"lm_head batch {batch} sampled rows")
+    b = batch - 1
+    Y1 = run_gemv(case.fmt, W, case.rows, case.cols, X[b:b + 1])
+    assert np.array_equal(Y[b:b + 1].view(np.uint32), Y1.view(np.uint32))
