@@ -527,6 +527,8 @@ def main():
     if not args.quick:
         # (workload, batch, variant): "" qgemv, "q8act" qgemv_q8act, "ws" qgemv_ws
         sweep = [("q8_0_256x1024", 1, ""), ("q6_k_151936x2048", 1, "")]
+        # the lm_head for two and four sequences
+        sweep += [("q6_k_151936x2048", b, "") for b in (2, 4)]
         sweep += [("q5_k_14336x4096", b, "") for b in (1, 4, 8)]
         sweep += [("q4_0_4096x14336", b, "") for b in (1, 4, 8)]
         # prefill-sized batches
